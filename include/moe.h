@@ -1,0 +1,156 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) mixture-of-experts feed-forward layer.
+ *
+ * The layer (per token x, already normalized by the block's pre-norm):
+ *   router   l = W_r x over the E routed and S shared experts ("A linear router scores
+ *            ... experts": "Qwen3.8-2.4T-A95B vs Inkling", component table, router row);
+ *   select   either the softmax top-k router (softmax over the routed experts, keep the
+ *            top k, renormalize; Qwen3.8 column of that row) or the sigmoid router with a
+ *            shared-expert sink (sigmoid scores, top-k of the routed experts steered by a
+ *            per-expert selection bias, weights normalized jointly over the k + S active
+ *            experts then multiplied by route_scale = k + S; Inkling column of that row,
+ *            and "Inkling vs Gemma 4 31B", component table, shared-expert row);
+ *   experts  SwiGLU FFNs E_j(x) = W_down,j (SiLU(W_gate,j x) * W_up,j x)
+ *            ("Inkling vs Gemma 4 31B", routed-expert row; SiLU per the Qwen3.8 2.4T A95B
+ *            atlas page, hidden_act);
+ *   combine  y = sum over active j of w_j E_j(x), optionally added to a residual
+ *            ("Qwen3.5-397B-A17B vs Inkling", block diagram, residual add after the MoE).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers to caller-owned, contiguous, row-major
+ *     buffers.  The library never allocates, frees or synchronizes; every call only
+ *     enqueues kernels on `stream` and returns.
+ *   - bf16 tensors hold IEEE bfloat16 bit patterns; f32 tensors IEEE binary32.  The
+ *     selection bias, logit offset, combine weights, outputs and the per-row expert
+ *     outputs are always f32.
+ *   - Layouts:  x [T, d];  w_router [E + S, d] (shared experts' rows last);
+ *     w_gate, w_up [E + S, I, d];  w_down [E + S, d, I];  every weight matrix is
+ *     contiguous along the reduction dimension.
+ *   - Rows: the T (k + S) expert-input rows are grouped by expert.  Group g < E holds the
+ *     tokens routed to expert g in ascending token order; group E + s (shared expert s)
+ *     holds every token in order, rows [T k + s T, T k + (s + 1) T).
+ *   - Pointers to tensors read with 16-byte vector loads (x, weights, y_rows, out,
+ *     residual, ws) must be 16-byte aligned; ws must be 256-byte aligned.
+ *   - Errors: argument problems are reported synchronously, before anything is enqueued
+ *     (MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE).  A failed launch returns
+ *     MOE_ERR_HIP.  T = 0 is a no-op returning MOE_OK.  No C++ exception crosses the ABI.
+ *   - Supported shapes: d % 256 == 0, I % 128 == 0, 1 <= k <= min(E, 32),
+ *     E + S <= 1024, 0 <= S <= 8; softmax requires S == 0 and route_scale == 1.
+ *   - Calls that share a workspace must be ordered on one stream.  The library holds no
+ *     global mutable state, so distinct streams with distinct workspaces are independent.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,          /* null/misaligned pointer, bad size or enum value */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid layer, but a shape this build does not tile */
+  MOE_ERR_WORKSPACE = 3,    /* ws_bytes below moe_workspace_size() */
+  MOE_ERR_HIP = 4           /* a kernel launch failed */
+} moe_status_t;
+
+typedef enum {
+  MOE_ROUTER_SOFTMAX_TOPK = 0,    /* softmax over E, top-k, renormalize (S must be 0) */
+  MOE_ROUTER_SIGMOID_SHARED = 1   /* sigmoid over E + S, bias-steered top-k, joint norm */
+} moe_router_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef struct {
+  int32_t d_model;         /* d: model width */
+  int32_t n_experts;       /* E: routed experts */
+  int32_t d_ff;            /* I: expert intermediate size */
+  int32_t top_k;           /* k: routed experts per token */
+  int32_t n_shared;        /* S: shared (always-active) experts; 0 for softmax */
+  int32_t router;          /* moe_router_t */
+  int32_t dtype;           /* moe_dtype_t of x, w_router and the expert weights */
+  int32_t bias_on_logits;  /* sigmoid router: 0 = selection bias added to the score
+                              sigmoid(l) (default reading), 1 = added to the logit */
+  float route_scale;       /* sigmoid: factor after the joint normalization (k + S);
+                              softmax: must be 1 */
+} moe_config_t;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* moe_status_str(moe_status_t status);
+
+/* Bytes of device workspace every entry point below needs for `T` tokens (host only,
+ * never touches the GPU).  The same workspace serves all entry points. */
+moe_status_t moe_workspace_size(const moe_config_t* cfg, int64_t T, size_t* bytes);
+
+/* Router: logits over the E + S experts with f32 accumulation of exact products,
+ * selection, and combine weights (definition: the router row of the component table of
+ * "Qwen3.8-2.4T-A95B vs Inkling"; shared-expert weighting: "Inkling vs Gemma 4 31B",
+ * shared-expert row).
+ *   x [T, d] (dtype), w_router [E + S, d] (dtype)
+ *   sel_bias [E] f32 or NULL: sigmoid router only; steers selection, not the weights
+ *   logit_offset [E] f32 or NULL: added to the routed experts' logits before scoring
+ *   topk_idx [T, k] int32 out: routed experts in descending selection score; equal
+ *            scores keep the lower index first
+ *   weights  [T, k + S] f32 out: the routed experts' weights in topk_idx order, then the
+ *            shared experts' weights; they sum to route_scale (sigmoid) or 1 (softmax)
+ *   ws: workspace of at least moe_workspace_size() bytes. */
+moe_status_t moe_route(const moe_config_t* cfg, int64_t T, const void* x,
+                       const void* w_router, const float* sel_bias,
+                       const float* logit_offset, int32_t* topk_idx, float* weights,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Grouping of the T (k + S) expert-input rows by expert: per-expert token histogram,
+ * exclusive prefix scan and a stable (ascending token) permutation.  This step is the
+ * GPU method's own; it has no counterpart on the pages.
+ *   topk_idx [T, k] int32 in: entries must lie in [0, E) and be distinct per token
+ *            (out-of-range entries are skipped and leave rows unassigned)
+ *   counts   [E + S] int32 out: rows per group (shared groups hold T)
+ *   offsets  [E + S + 1] int32 out: exclusive prefix of counts; offsets[E + S] = T(k + S)
+ *   row_token [T (k + S)] int32 out: token of each grouped row
+ *   slot_row  [T (k + S)] int32 out: slot_row[t (k + S) + j] = row of token t's j-th
+ *             active expert (j < k routed in topk_idx order, then the shared experts) */
+moe_status_t moe_permute(const moe_config_t* cfg, int64_t T, const int32_t* topk_idx,
+                         int32_t* counts, int32_t* offsets, int32_t* row_token,
+                         int32_t* slot_row, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Grouped SwiGLU experts over the grouped rows ("Inkling vs Gemma 4 31B", routed- and
+ * shared-expert rows): for every group g and each of its rows r (token t = row_token[r]),
+ *   h = SiLU(W_gate,g x_t) * (W_up,g x_t)      (f32 accumulation; bf16 dtype rounds h to
+ *                                                bf16 once, to nearest even)
+ *   y_rows[r] = W_down,g h                      (f32 accumulation, f32 out)
+ *   offsets [E + S + 1], row_token [T (k + S)]: as produced by moe_permute
+ *   y_rows [T (k + S), d] f32 out. */
+moe_status_t moe_grouped_swiglu(const moe_config_t* cfg, int64_t T, const void* x,
+                                const int32_t* offsets, const int32_t* row_token,
+                                const void* w_gate, const void* w_up, const void* w_down,
+                                float* y_rows, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* Weighted combine back to token order, reading each token's k + S rows (no scatter):
+ *   out[t] = [residual[t] +] sum_{j < k + S} weights[t, j] * y_rows[slot_row[t (k+S) + j]]
+ * summed in the fixed order j = 0 .. k + S - 1 ("Qwen3.5-397B-A17B vs Inkling", block
+ * diagram, residual add).  residual [T, d] f32 or NULL; out [T, d] f32. */
+moe_status_t moe_combine(const moe_config_t* cfg, int64_t T, const float* y_rows,
+                         const int32_t* slot_row, const float* weights,
+                         const float* residual, float* out, hipStream_t stream);
+
+/* The whole layer: route, group, grouped SwiGLU experts, combine, on one stream.
+ *   out [T, d] f32; residual [T, d] f32 or NULL;
+ *   topk_idx_out [T, k] int32 or NULL, counts_out [E + S] int32 or NULL: optional copies
+ *   of the routing for inspection. */
+moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x,
+                         const void* w_router, const float* sel_bias,
+                         const float* logit_offset, const void* w_gate, const void* w_up,
+                         const void* w_down, const float* residual, float* out,
+                         int32_t* topk_idx_out, int32_t* counts_out, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,61 @@
+// Weighted combine of the expert outputs back into token order on gfx950.
+//
+// out[t] = [residual[t] +] sum_{j < A} w[t, j] * y_rows[slot_row[t A + j]], A = k + S, in
+// the fixed order j = 0 .. A - 1 (the MoE branch output that rejoins the residual stream:
+// "Qwen3.5-397B-A17B vs Inkling", block diagram, residual add after the experts).
+// Each token gathers its A rows (no scatter, no atomics); every access is a coalesced
+// 16-byte vector access along d.
+#include "moe_device.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+constexpr int kMaxActive = 64;
+
+__global__ __launch_bounds__(256) void combine_kernel(
+    const float4* __restrict__ y_rows, const int32_t* __restrict__ slot_row,
+    const float* __restrict__ weights, const float4* __restrict__ residual,
+    float4* __restrict__ out, int d4, int A, int R) {
+  __shared__ int32_t rows[kMaxActive];
+  __shared__ float wts[kMaxActive];
+  const int t = blockIdx.x;
+  if (threadIdx.x < A) {
+    const int r = slot_row[(size_t)t * A + threadIdx.x];
+    rows[threadIdx.x] = min(max(r, 0), R - 1);
+    wts[threadIdx.x] = weights[(size_t)t * A + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c = blockIdx.y * blockDim.x + threadIdx.x; c < d4; c += gridDim.y * blockDim.x) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < A; ++j) {
+      const float4 v = y_rows[(size_t)rows[j] * d4 + c];
+      const float w = wts[j];
+      acc.x = fmaf(w, v.x, acc.x);
+      acc.y = fmaf(w, v.y, acc.y);
+      acc.z = fmaf(w, v.z, acc.z);
+      acc.w = fmaf(w, v.w, acc.w);
+    }
+    if (residual != nullptr) {
+      const float4 r = residual[(size_t)t * d4 + c];
+      acc.x = r.x + acc.x;
+      acc.y = r.y + acc.y;
+      acc.z = r.z + acc.z;
+      acc.w = r.w + acc.w;
+    }
+    out[(size_t)t * d4 + c] = acc;
+  }
+}
+
+hipError_t launch_combine(const float* y_rows, const int32_t* slot_row, const float* weights,
+                          const float* residual, float* out, int T, int d, int A, int R,
+                          hipStream_t stream) {
+  const int d4 = d / 4;
+  const int ysplit = (d4 + 1023) / 1024;  // at most 4 float4 per thread
+  hipLaunchKernelGGL(combine_kernel, dim3(T, ysplit), dim3(256), 0, stream,
+                     reinterpret_cast<const float4*>(y_rows), slot_row, weights,
+                     reinterpret_cast<const float4*>(residual),
+                     reinterpret_cast<float4*>(out), d4, A, R);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,61 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer: storage types,
+// bf16 conversion, MFMA operand types and wave-wide reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;  // CDNA wavefront width
+constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, 32 CUs each
+
+// bf16 is stored as its raw 16-bit pattern.
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Monotone map of an f32 onto uint32: a < b  <=>  key(a) < key(b) (no NaNs).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, kWave);
+    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, kWave);
+    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Workgroup id remap so that the workgroups the dispatcher places on one XCD
+// (consecutive ids go round-robin over the 8 XCDs) receive a contiguous range of
+// logical tile ids, which then share that XCD's L2.  A bijection on [0, n).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t p, uint32_t n) {
+  uint32_t xcd = p % kXcds, j = p / kXcds;
+  uint32_t q = n / kXcds, r = n % kXcds;
+  return xcd * q + (xcd < r ? xcd : r) + j;
+}
+
+}  // namespace moe

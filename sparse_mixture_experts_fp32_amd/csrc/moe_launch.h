@@ -1,0 +1,53 @@
+// Host-side launchers of the MoE layer's gfx950 kernels (internal to the library).
+// Arguments are validated by the C-ABI layer before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tile sizes of the grouped expert GEMMs, shared with the workspace planner.
+constexpr int kGemmBM = 128;        // grouped rows per tile
+constexpr int kGateUpBN = 128;      // h columns per gate/up tile (128 gate + 128 up rows)
+constexpr int kDownBN = 256;        // y columns per down tile
+constexpr int kPermBlock = 256;     // tokens per permute block
+constexpr int kRouterTile = 64;     // tokens and experts per router tile
+
+struct PlanEntry {   // one m-tile of the grouped GEMM
+  int32_t group, row0, nrows, pad;
+};
+
+// Router partial logits: part[s][t][e] = sum over the s-th K chunk of x[t] . w_router[e].
+hipError_t launch_router_logits(int dtype, const void* x, const void* w_router, float* part,
+                                int T, int d, int NE, int nsplit, int kchunk,
+                                hipStream_t stream);
+
+// Selection and combine weights from the partial logits (summed in split order).
+hipError_t launch_topk(const float* part, int nsplit, int T, int E, int S, int k,
+                       int router, int bias_on_logits, float route_scale,
+                       const float* sel_bias, const float* logit_offset, int32_t* topk_idx,
+                       float* weights, hipStream_t stream);
+
+// Histogram, scan and stable scatter of the grouped rows.
+hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int S, int k,
+                          int32_t* block_hist, int32_t* counts, int32_t* offsets,
+                          int32_t* row_token, int32_t* slot_row, hipStream_t stream);
+
+// Grouped gate/up (+SwiGLU) and down GEMMs.  h is [R, I] (dtype), y_rows [R, d] f32.
+hipError_t launch_grouped_swiglu(int dtype, const void* x, const int32_t* offsets,
+                                 const int32_t* row_token, const void* w_gate,
+                                 const void* w_up, const void* w_down, void* h,
+                                 float* y_rows, PlanEntry* plan, int T, int d, int I, int G,
+                                 int R, hipStream_t stream);
+
+// Weighted combine of each token's A = k + S rows, fixed order, optional residual.
+hipError_t launch_combine(const float* y_rows, const int32_t* slot_row, const float* weights,
+                          const float* residual, float* out, int T, int d, int A, int R,
+                          hipStream_t stream);
+
+// Upper bound of the grouped GEMM's m-tiles for R rows in G groups.
+inline int64_t max_mtiles(int64_t R, int64_t G) { return R / kGemmBM + G; }
+
+}  // namespace moe

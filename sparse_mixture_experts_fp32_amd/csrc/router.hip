@@ -1,0 +1,245 @@
+// Router of the MoE layer on gfx950: logits l = W_r x with f32 accumulation, then a
+// wavefront-wide top-k and the combine weights.
+//
+// Definition followed: the router row of the component table of "Qwen3.8-2.4T-A95B vs
+// Inkling" (a linear router; softmax top-k with renormalization for Qwen3.8; sigmoid
+// scores over routed + shared experts, bias-steered top-k and weights normalized jointly
+// over the active experts then multiplied by their count for Inkling) and the
+// shared-expert row of "Inkling vs Gemma 4 31B" (each shared expert weighted by its own
+// router score).
+#include "moe_device.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------------------
+// Logits.  One workgroup (4 waves) owns 64 tokens x 64 experts of one K chunk; each wave
+// a 32 x 32 block as 2 x 2 MFMA tiles.  bf16 products are exact in f32, so the only
+// rounding is the f32 accumulation.  Operands go straight from global memory (x rows and
+// router rows are reused out of L2) into the MFMA register layout; no LDS.
+// Two accumulator sets (even / odd K steps) halve the length of each f32 sum.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_logits_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ part,
+    int T, int d, int NE, int kchunk) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * kRouterTile + (wave & 1) * 32;
+  const int e0 = blockIdx.y * kRouterTile + (wave >> 1) * 32;
+  const int split = blockIdx.z;
+  const int kbeg = split * kchunk;
+  const int kend = min(d, kbeg + kchunk);
+  // v_mfma_f32_16x16x32_bf16 operands: lane l holds row (l % 16), K elements
+  // [8 (l / 16), 8 (l / 16) + 8) of its 32-wide K step.
+  const int r = lane & 15, kq = (lane >> 4) * 8;
+  const uint16_t* a0 = x + (size_t)min(t0 + r, T - 1) * d + kq;
+  const uint16_t* a1 = x + (size_t)min(t0 + 16 + r, T - 1) * d + kq;
+  const uint16_t* b0 = wr + (size_t)min(e0 + r, NE - 1) * d + kq;
+  const uint16_t* b1 = wr + (size_t)min(e0 + 16 + r, NE - 1) * d + kq;
+  f32x4 c[2][2][2] = {};
+  int k = kbeg;
+  for (; k + 64 <= kend; k += 64) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 A0 = *reinterpret_cast<const bf16x8*>(a0 + k + 32 * h);
+      bf16x8 A1 = *reinterpret_cast<const bf16x8*>(a1 + k + 32 * h);
+      bf16x8 B0 = *reinterpret_cast<const bf16x8*>(b0 + k + 32 * h);
+      bf16x8 B1 = *reinterpret_cast<const bf16x8*>(b1 + k + 32 * h);
+      c[h][0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0, c[h][0][0], 0, 0, 0);
+      c[h][0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B1, c[h][0][1], 0, 0, 0);
+      c[h][1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, c[h][1][0], 0, 0, 0);
+      c[h][1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B1, c[h][1][1], 0, 0, 0);
+    }
+  }
+  if (k < kend) {  // one trailing 32-wide step
+    bf16x8 A0 = *reinterpret_cast<const bf16x8*>(a0 + k);
+    bf16x8 A1 = *reinterpret_cast<const bf16x8*>(a1 + k);
+    bf16x8 B0 = *reinterpret_cast<const bf16x8*>(b0 + k);
+    bf16x8 B1 = *reinterpret_cast<const bf16x8*>(b1 + k);
+    c[0][0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0, c[0][0][0], 0, 0, 0);
+    c[0][0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B1, c[0][0][1], 0, 0, 0);
+    c[0][1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, c[0][1][0], 0, 0, 0);
+    c[0][1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B1, c[0][1][1], 0, 0, 0);
+  }
+  // Result layout: lane l holds column (l % 16), rows 4 (l / 16) + i.
+  float* out = part + (size_t)split * T * NE;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int t = t0 + 16 * mi + 4 * (lane >> 4) + i;
+        int e = e0 + 16 * ni + (lane & 15);
+        if (t < T && e < NE) out[(size_t)t * NE + e] = c[0][mi][ni][i] + c[1][mi][ni][i];
+      }
+}
+
+// f32 inputs: the same tiling on v_mfma_f32_16x16x4_f32 (lane l holds row l % 16,
+// K element l / 16 of each 4-wide step).
+__global__ __launch_bounds__(256) void router_logits_f32(
+    const float* __restrict__ x, const float* __restrict__ wr, float* __restrict__ part,
+    int T, int d, int NE, int kchunk) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * kRouterTile + (wave & 1) * 32;
+  const int e0 = blockIdx.y * kRouterTile + (wave >> 1) * 32;
+  const int split = blockIdx.z;
+  const int kbeg = split * kchunk;
+  const int kend = min(d, kbeg + kchunk);
+  const int r = lane & 15, kq = lane >> 4;
+  const float* a0 = x + (size_t)min(t0 + r, T - 1) * d + kq;
+  const float* a1 = x + (size_t)min(t0 + 16 + r, T - 1) * d + kq;
+  const float* b0 = wr + (size_t)min(e0 + r, NE - 1) * d + kq;
+  const float* b1 = wr + (size_t)min(e0 + 16 + r, NE - 1) * d + kq;
+  f32x4 c[2][2] = {};
+  for (int k = kbeg; k < kend; k += 4) {
+    float A0 = a0[k], A1 = a1[k], B0 = b0[k], B1 = b1[k];
+    c[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(A0, B0, c[0][0], 0, 0, 0);
+    c[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(A0, B1, c[0][1], 0, 0, 0);
+    c[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(A1, B0, c[1][0], 0, 0, 0);
+    c[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(A1, B1, c[1][1], 0, 0, 0);
+  }
+  float* out = part + (size_t)split * T * NE;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int t = t0 + 16 * mi + 4 * (lane >> 4) + i;
+        int e = e0 + 16 * ni + (lane & 15);
+        if (t < T && e < NE) out[(size_t)t * NE + e] = c[mi][ni][i];
+      }
+}
+
+hipError_t launch_router_logits(int dtype, const void* x, const void* w_router, float* part,
+                                int T, int d, int NE, int nsplit, int kchunk,
+                                hipStream_t stream) {
+  dim3 grid((T + kRouterTile - 1) / kRouterTile, (NE + kRouterTile - 1) / kRouterTile,
+            nsplit);
+  if (dtype == 1)
+    hipLaunchKernelGGL(router_logits_bf16, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
+                       part, T, d, NE, kchunk);
+  else
+    hipLaunchKernelGGL(router_logits_f32, grid, dim3(256), 0, stream,
+                       static_cast<const float*>(x), static_cast<const float*>(w_router), part,
+                       T, d, NE, kchunk);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Selection.  One wave per token; lane l holds experts l, l + 64, ...  Each of the k
+// rounds takes the wave-wide maximum of 64-bit keys (order-preserving f32 bits of the
+// selection score in the high word, the inverted expert index in the low word, so equal
+// scores resolve to the lower index) and retires the winner.
+//   sigmoid: s = 1 / (1 + exp(-l)); selection score s + b (or sigmoid(l + b) when the
+//            bias applies to the logit); weight route_scale * s_j / sum over the active
+//            set (routed in selection order, then shared) of s.
+//   softmax: selection on the logit (monotone in the probability); weight
+//            exp(l_j - l_top) / sum over the top k of exp(l_i - l_top), which equals the
+//            renormalized softmax probability.
+// ---------------------------------------------------------------------------------------
+template <int MAXV>
+__global__ __launch_bounds__(256) void topk_kernel(
+    const float* __restrict__ part, int nsplit, int T, int E, int S, int k, int router,
+    int bias_on_logits, float route_scale, const float* __restrict__ sel_bias,
+    const float* __restrict__ logit_offset, int32_t* __restrict__ topk_idx,
+    float* __restrict__ weights) {
+  __shared__ float sval[4][64];
+  __shared__ float sden[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  const int NE = E + S;
+  const bool live = t < T;
+  float raw[MAXV];
+  uint64_t key[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = lane + 64 * i;
+    raw[i] = 0.f;
+    key[i] = 0;
+    if (live && e < NE) {
+      float l = 0.f;
+      for (int s = 0; s < nsplit; ++s) l += part[((size_t)s * T + t) * NE + e];
+      if (logit_offset != nullptr && e < E) l += logit_offset[e];
+      float sel;
+      if (router == 1) {
+        const float sc = 1.0f / (1.0f + expf(-l));
+        raw[i] = sc;
+        const float b = (sel_bias != nullptr && e < E) ? sel_bias[e] : 0.0f;
+        sel = bias_on_logits ? 1.0f / (1.0f + expf(-(l + b))) : sc + b;
+      } else {
+        raw[i] = l;
+        sel = l;
+      }
+      if (e < E)
+        key[i] = (static_cast<uint64_t>(f32_order_key(sel)) << 32) |
+                 (0xffffffffu - static_cast<uint32_t>(e));
+    }
+  }
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
+    if (live && lane == (e & 63)) {
+      const int slot = e >> 6;
+      float v = 0.f;
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i)
+        if (i == slot) {
+          v = raw[i];
+          key[i] = 0;
+        }
+      sval[wave][j] = v;
+      topk_idx[(size_t)t * k + j] = e;
+    }
+  }
+  // Shared experts' raw scores follow the routed ones.
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = lane + 64 * i;
+    if (live && e >= E && e < NE) sval[wave][k + (e - E)] = raw[i];
+  }
+  __syncthreads();
+  const int A = k + S;
+  if (live && lane == 0) {
+    float den = 0.f;
+    if (router == 1) {
+      for (int j = 0; j < A; ++j) den += sval[wave][j];
+    } else {
+      const float top = sval[wave][0];
+      for (int j = 0; j < A; ++j) den += expf(sval[wave][j] - top);
+    }
+    sden[wave] = den;
+  }
+  __syncthreads();
+  if (live && lane < A) {
+    const float den = sden[wave];
+    const float v = sval[wave][lane];
+    const float w = (router == 1) ? route_scale * v / den : expf(v - sval[wave][0]) / den;
+    weights[(size_t)t * A + lane] = w;
+  }
+}
+
+hipError_t launch_topk(const float* part, int nsplit, int T, int E, int S, int k, int router,
+                       int bias_on_logits, float route_scale, const float* sel_bias,
+                       const float* logit_offset, int32_t* topk_idx, float* weights,
+                       hipStream_t stream) {
+  const int per_lane = (E + S + 63) / 64;
+  dim3 grid((T + 3) / 4);
+#define MOE_TOPK(MV)                                                                      \
+  hipLaunchKernelGGL(topk_kernel<MV>, grid, dim3(256), 0, stream, part, nsplit, T, E, S, \
+                     k, router, bias_on_logits, route_scale, sel_bias, logit_offset,      \
+                     topk_idx, weights)
+  if (per_lane <= 1) MOE_TOPK(1);
+  else if (per_lane <= 2) MOE_TOPK(2);
+  else if (per_lane <= 4) MOE_TOPK(4);
+  else if (per_lane <= 8) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,84 @@
+"""Helpers of the GPU tests and the bench: host arrays <-> device tensors, config
+structs, and calls of the library through its C ABI.  Marshalling only."""
+from __future__ import annotations
+
+import numpy as np
+
+import sparse_mixture_experts_fp32_amd as M
+
+
+def cfg_struct(c) -> "M.moe_config_t":
+    return M.make_config(c.d, c.E, c.I, c.k, c.S, c.router, c.dtype,
+                         bias_on_logits=c.bias_on_logits, route_scale=c.route_scale)
+
+
+def to_dev(a: np.ndarray | None, torch):
+    """Host array -> device tensor; bf16 bit patterns (uint16) become torch.bfloat16."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(a).to("cuda")
+
+
+def expert_tensor_to_dev(arr: np.ndarray, torch, chunk: int = 16):
+    """Upload a large [E + S, ...] expert tensor chunk by chunk (bounded host temporaries)."""
+    dt = torch.bfloat16 if arr.dtype == np.uint16 else torch.float32
+    out = torch.empty(arr.shape, dtype=dt, device="cuda")
+    for e0 in range(0, arr.shape[0], chunk):
+        part = torch.from_numpy(np.ascontiguousarray(arr[e0:e0 + chunk]))
+        if arr.dtype == np.uint16:
+            part = part.view(torch.bfloat16)
+        out[e0:e0 + chunk].copy_(part)
+    return out
+
+
+def device_inputs(inputs: dict, torch) -> dict:
+    d = {}
+    for k, v in inputs.items():
+        if k in ("w_gate", "w_up", "w_down"):
+            d[k] = expert_tensor_to_dev(v, torch)
+        else:
+            d[k] = to_dev(v, torch)
+    return d
+
+
+def workspace(cfg, T, torch):
+    n = M.moe_workspace_size(cfg, T)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda"), n
+
+
+def run_forward(c, dev: dict, torch, residual=None, ws=None):
+    """moe_forward on device tensors; returns (out, topk_idx, counts) device tensors."""
+    cfg = cfg_struct(c)
+    T = dev["x"].shape[0]
+    if ws is None:
+        ws = workspace(cfg, T, torch)
+    buf, n = ws
+    out = torch.empty((T, c.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, c.k), dtype=torch.int32, device="cuda")
+    counts = torch.empty((c.E + c.S,), dtype=torch.int32, device="cuda")
+    M.moe_forward(cfg, T, dev["x"], dev["w_router"], dev.get("sel_bias"),
+                  dev.get("logit_offset"), dev["w_gate"], dev["w_up"], dev["w_down"],
+                  residual, out, idx, counts, buf, n)
+    return out, idx, counts
+
+
+def host_grouping(idx: np.ndarray, E: int, S: int):
+    """Rows grouped by expert from a host-side selection (ascending token order within a
+    group, shared experts' groups last): the layout the library's permute produces."""
+    T, k = idx.shape
+    A = k + S
+    flat = idx.ravel()
+    tok = np.repeat(np.arange(T), k)
+    slot = np.tile(np.arange(k), T)
+    order = np.argsort(flat, kind="stable")           # by expert, then token
+    counts = np.concatenate([np.bincount(flat, minlength=E), np.full(S, T)])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    row_token = np.concatenate([tok[order]] + [np.arange(T)] * S).astype(np.int32)
+    slot_row = np.empty((T, A), np.int32)
+    slot_row[tok[order], slot[order]] = np.arange(T * k)
+    for s in range(S):
+        slot_row[:, k + s] = T * k + s * T + np.arange(T)
+    return counts.astype(np.int32), offsets, row_token, slot_row

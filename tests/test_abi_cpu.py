@@ -1,0 +1,132 @@
+"""The C ABI on the host: the library loads, exports every function include/moe.h
+declares, sizes workspaces, and rejects bad arguments before touching the GPU.  No
+compute call is made."""
+import ctypes
+import os
+
+import pytest
+
+import sparse_mixture_experts_fp32_amd as M
+from moe_inputs import CONFIGS, CONFIG_ORDER
+
+pytestmark = pytest.mark.skipif(not os.path.exists(M.LIB_PATH),
+                                reason="libmoe.so not built (run __graft_entry__.build())")
+
+# Plausible-looking aligned device addresses: every call below fails validation before
+# any of them would be dereferenced or handed to HIP.
+A = 0x7F0000000000
+
+
+def cfg_of(c, **kw):
+    args = dict(d_model=c.d, n_experts=c.E, d_ff=c.I, top_k=c.k, n_shared=c.S,
+                router=c.router, dtype=c.dtype)
+    args.update(kw)
+    return M.make_config(**args)
+
+
+def test_library_exports_every_declared_function():
+    lib = M.load_library()
+    names = M.header_functions()
+    assert set(names) == {"moe_status_str", "moe_workspace_size", "moe_route", "moe_permute",
+                          "moe_grouped_swiglu", "moe_combine", "moe_forward"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(5):
+        assert M.status_str(s).startswith("MOE_")
+    assert "UNKNOWN" in M.status_str(99)
+
+
+@pytest.mark.parametrize("name", CONFIG_ORDER)
+def test_workspace_size_covers_the_intermediates(name):
+    c = CONFIGS[name]
+    cfg = cfg_of(c)
+    ws = M.moe_workspace_size(cfg, c.T)
+    esize = 2 if c.dtype == "bf16" else 4
+    rows = c.T * (c.k + c.S)
+    assert ws >= rows * c.d * 4 + rows * c.I * esize       # y_rows (f32) + h
+    assert M.moe_workspace_size(cfg, 0) < ws
+    assert M.moe_workspace_size(cfg, c.T + 1) >= ws
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(top_k=0), M.MOE_ERR_ARG),
+    (dict(top_k=300), M.MOE_ERR_ARG),
+    (dict(n_shared=-1), M.MOE_ERR_ARG),
+    (dict(router=7), M.MOE_ERR_ARG),
+    (dict(dtype=5), M.MOE_ERR_ARG),
+    (dict(route_scale=0.0), M.MOE_ERR_ARG),
+    (dict(route_scale=float("nan")), M.MOE_ERR_ARG),
+    (dict(d_model=6000), M.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff=3000), M.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=33, n_experts=256), M.MOE_ERR_UNSUPPORTED),
+    (dict(n_experts=1020, n_shared=8), M.MOE_ERR_UNSUPPORTED),
+])
+def test_config_validation(bad, status):
+    cfg = cfg_of(CONFIGS["inkling_decode"], **bad)
+    with pytest.raises(M.MoEError) as ei:
+        M.moe_workspace_size(cfg, 32)
+    assert ei.value.status == status
+
+
+def test_softmax_router_rejects_shared_experts_and_scale():
+    c = CONFIGS["qwen38"]
+    with pytest.raises(M.MoEError) as ei:
+        M.moe_workspace_size(cfg_of(c, n_shared=1), 8)
+    assert ei.value.status == M.MOE_ERR_ARG
+    with pytest.raises(M.MoEError):
+        M.moe_workspace_size(cfg_of(c, route_scale=2.0), 8)
+
+
+def test_entry_points_validate_before_launch():
+    c = CONFIGS["inkling_decode"]
+    cfg = cfg_of(c)
+    T = c.T
+    need = M.moe_workspace_size(cfg, T)
+
+    def status(fn, *args):
+        with pytest.raises(M.MoEError) as ei:
+            fn(*args, stream=0)
+        return ei.value.status
+
+    # null / misaligned pointers
+    assert status(M.moe_route, cfg, T, None, A, None, None, A, A, A, need) == M.MOE_ERR_ARG
+    assert status(M.moe_route, cfg, T, A + 2, A, None, None, A, A, A, need) == M.MOE_ERR_ARG
+    assert status(M.moe_route, cfg, T, A, A, None, None, A, A, A + 64, need) == M.MOE_ERR_ARG
+    # workspace too small
+    assert status(M.moe_route, cfg, T, A, A, None, None, A, A, A, need - 1) == \
+        M.MOE_ERR_WORKSPACE
+    assert status(M.moe_permute, cfg, T, A, A, A, A, A, A, 16) == M.MOE_ERR_WORKSPACE
+    assert status(M.moe_permute, cfg, T, A, None, A, A, A, A, need) == M.MOE_ERR_ARG
+    assert status(M.moe_grouped_swiglu, cfg, T, A, A, A, A, A, A, A, A, 0) == \
+        M.MOE_ERR_WORKSPACE
+    assert status(M.moe_grouped_swiglu, cfg, T, A, A, A, A, A + 8, A, A, A, need) == \
+        M.MOE_ERR_ARG
+    assert status(M.moe_combine, cfg, T, A, A, None, None, A) == M.MOE_ERR_ARG
+    assert status(M.moe_combine, cfg, T, A, A, A, A + 4, A) == M.MOE_ERR_ARG
+    assert status(M.moe_forward, cfg, T, A, A, None, None, A, A, A, None, A, None, None,
+                  A, 1) == M.MOE_ERR_WORKSPACE
+    assert status(M.moe_forward, cfg, -1, A, A, None, None, A, A, A, None, A, None, None,
+                  A, need) == M.MOE_ERR_ARG
+    # a selection bias only exists for the sigmoid router
+    q = CONFIGS["qwen38"]
+    qcfg = cfg_of(q)
+    qneed = M.moe_workspace_size(qcfg, 8)
+    assert status(M.moe_route, qcfg, 8, A, A, A, None, A, A, A, qneed) == M.MOE_ERR_ARG
+
+
+def test_zero_tokens_is_a_no_op():
+    cfg = cfg_of(CONFIGS["inkling_decode"])
+    # T = 0 returns before any pointer is looked at and before any HIP call.
+    M.moe_forward(cfg, 0, None, None, None, None, None, None, None, None, None, None, None,
+                  None, 0, stream=0)
+    M.moe_route(cfg, 0, None, None, None, None, None, None, None, 0, stream=0)
+    M.moe_permute(cfg, 0, None, None, None, None, None, None, 0, stream=0)
+    M.moe_grouped_swiglu(cfg, 0, None, None, None, None, None, None, None, None, 0, stream=0)
+    M.moe_combine(cfg, 0, None, None, None, None, None, stream=0)
+
+
+def test_config_struct_layout_matches_header():
+    assert ctypes.sizeof(M.moe_config_t) == 9 * 4

@@ -1,0 +1,231 @@
+"""Parity of the GPU layer (through the C ABI) with the CPU oracle on seeded inputs.
+
+Small shapes are compared element by element (they span several tiles, ragged tails,
+expert counts that are not multiples of 64, k = E, the largest expert count, one token).
+Each entry point is also checked on its own with host-made inputs.  The full-size
+workloads are compared on all routing decisions and on sampled tokens' outputs."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import sparse_mixture_experts_fp32_amd as M  # noqa: E402
+from gpu_util import (cfg_struct, device_inputs, host_grouping, run_forward,  # noqa: E402
+                      to_dev, workspace)
+from moe_inputs import CONFIGS, MoEConfig, make_inputs  # noqa: E402
+from oracle import moe_oracle as O  # noqa: E402
+from parity import assert_outputs, check_routing, output_metrics  # noqa: E402
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def small(name, router, dtype, T, d, E, S, I, k, w_std=0.05, seed=10, bias_std=0.1):
+    sig = router == "sigmoid"
+    return MoEConfig(name=name, T=T, d=d, E=E, S=S if sig else 0, I=I, k=k, router=router,
+                     dtype=dtype, x_std=1.0, w_std=w_std, bias_std=bias_std if sig else 0.0,
+                     zipf_s=0.0, zipf_hot_share=0.0, seed=seed)
+
+
+SMALL = {c.name: c for c in [
+    CONFIGS["tiny_fp32"],
+    small("sig_bf16", "sigmoid", "bf16", T=300, d=512, E=40, S=2, I=256, k=6),
+    small("soft_bf16", "softmax", "bf16", T=257, d=768, E=64, S=0, I=384, k=8, seed=11),
+    small("sig_f32", "sigmoid", "f32", T=100, d=256, E=20, S=3, I=128, k=4, seed=12),
+    small("soft_bf16_k_eq_E", "softmax", "bf16", T=70, d=256, E=8, S=0, I=128, k=8, seed=13),
+    small("sig_bf16_big_groups", "sigmoid", "bf16", T=1000, d=256, E=8, S=1, I=256, k=2,
+          seed=14),
+    small("sig_bf16_max_experts", "sigmoid", "bf16", T=64, d=256, E=1016, S=8, I=128, k=32,
+          seed=15),
+    small("soft_f32_one_token", "softmax", "f32", T=1, d=256, E=16, S=0, I=128, k=2,
+          seed=16),
+    small("sig_bf16_logit_bias", "sigmoid", "bf16", T=200, d=512, E=48, S=2, I=128, k=6,
+          seed=17).with_(bias_on_logits=True),
+]}
+
+_cache = {}
+
+
+def inputs_of(c):
+    if c.name not in _cache:
+        _cache.clear()
+        inp = make_inputs(c)
+        _cache[c.name] = (inp, device_inputs(inp, torch))
+    return _cache[c.name]
+
+
+def mode_of(c):
+    return "bf16_flow" if c.dtype == "bf16" else "exact"
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(name):
+    c = SMALL[name]
+    inp, dev = inputs_of(c)
+    out, idx, counts = run_forward(c, dev, torch)
+    torch.cuda.synchronize()
+    out, idx, counts = out.cpu().numpy(), idx.cpu().numpy(), counts.cpu().numpy()
+    ref = O.moe_forward(c, inp, mode=mode_of(c))
+    excl = check_routing(idx, ref.routing, c.E)
+    assert (counts[:c.E] == np.bincount(idx.ravel(), minlength=c.E)).all()
+    assert (counts[c.E:] == c.T).all()
+    mx, mn = assert_outputs(out[~excl], ref.y[~excl], f"{name} forward")
+    log(f"{name}: excluded {excl.sum()}/{c.T}, max rel {mx:.2e}, mean rel {mn:.2e}")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_route_stage(name):
+    c = SMALL[name]
+    inp, dev = inputs_of(c)
+    cfg = cfg_struct(c)
+    buf, n = workspace(cfg, c.T, torch)
+    idx = torch.empty((c.T, c.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((c.T, c.k + c.S), dtype=torch.float32, device="cuda")
+    M.moe_route(cfg, c.T, dev["x"], dev["w_router"], dev.get("sel_bias"),
+                dev.get("logit_offset"), idx, w, buf, n)
+    torch.cuda.synchronize()
+    idx, w = idx.cpu().numpy(), w.cpu().numpy()
+    r = O.route(c, inp["x"], inp["w_router"], inp["sel_bias"], inp["logit_offset"])
+    excl = check_routing(idx, r, c.E)
+    ok = ~excl
+    # Weights follow the selection order; compare where the sets agree.
+    np.testing.assert_allclose(w.sum(1), c.route_scale, rtol=2e-6)
+    same_order = (idx == r.idx).all(1) & ok
+    np.testing.assert_allclose(w[same_order], r.weights[same_order], rtol=2e-5, atol=0)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_permute_stage(name):
+    """Grouping of a host (oracle) selection, bit-exact against a stable host sort."""
+    c = SMALL[name]
+    inp, dev = inputs_of(c)
+    r = O.route(c, inp["x"], inp["w_router"], inp["sel_bias"], inp["logit_offset"])
+    want = host_grouping(r.idx, c.E, c.S)
+    cfg = cfg_struct(c)
+    buf, n = workspace(cfg, c.T, torch)
+    A, G = c.k + c.S, c.E + c.S
+    idx = to_dev(r.idx.astype(np.int32), torch)
+    counts = torch.full((G,), -1, dtype=torch.int32, device="cuda")
+    offsets = torch.full((G + 1,), -1, dtype=torch.int32, device="cuda")
+    row_token = torch.full((c.T * A,), -1, dtype=torch.int32, device="cuda")
+    slot_row = torch.full((c.T * A,), -1, dtype=torch.int32, device="cuda")
+    M.moe_permute(cfg, c.T, idx, counts, offsets, row_token, slot_row, buf, n)
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy() for t in (counts, offsets, row_token, slot_row)]
+    for g_, w_, what in zip(got, want, ("counts", "offsets", "row_token", "slot_row")):
+        assert (g_.reshape(w_.shape) == w_).all(), what
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_grouped_swiglu_stage(name):
+    """Per-row expert outputs from a host grouping, against the oracle's SwiGLU expert."""
+    c = SMALL[name]
+    inp, dev = inputs_of(c)
+    r = O.route(c, inp["x"], inp["w_router"], inp["sel_bias"], inp["logit_offset"])
+    counts, offsets, row_token, _ = host_grouping(r.idx, c.E, c.S)
+    cfg = cfg_struct(c)
+    buf, n = workspace(cfg, c.T, torch)
+    R = c.T * (c.k + c.S)
+    y = torch.empty((R, c.d), dtype=torch.float32, device="cuda")
+    M.moe_grouped_swiglu(cfg, c.T, dev["x"], to_dev(offsets, torch), to_dev(row_token, torch),
+                         dev["w_gate"], dev["w_up"], dev["w_down"], y, buf, n)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    ref = np.zeros((R, c.d))
+    x64 = O.promote(inp["x"], c.dtype)
+    for g in range(c.E + c.S):
+        r0, r1 = offsets[g], offsets[g + 1]
+        if r1 == r0:
+            continue
+        ref[r0:r1] = O.swiglu_expert(x64[row_token[r0:r1]],
+                                     O.promote(inp["w_gate"][g], c.dtype),
+                                     O.promote(inp["w_up"][g], c.dtype),
+                                     O.promote(inp["w_down"][g], c.dtype),
+                                     c.dtype == "bf16")
+    assert_outputs(y, ref, f"{name} y_rows")
+
+
+@pytest.mark.parametrize("name", ["sig_bf16", "soft_bf16", "tiny_fp32"])
+def test_combine_stage(name):
+    c = SMALL[name]
+    inp, _ = inputs_of(c)
+    r = O.route(c, inp["x"], inp["w_router"], inp["sel_bias"], inp["logit_offset"])
+    _, _, _, slot_row = host_grouping(r.idx, c.E, c.S)
+    R = c.T * (c.k + c.S)
+    rng = np.random.default_rng(7)
+    y_rows = rng.standard_normal((R, c.d)).astype(np.float32)
+    resid = rng.standard_normal((c.T, c.d)).astype(np.float32)
+    w = r.weights.astype(np.float32)
+    cfg = cfg_struct(c)
+    for use_res in (False, True):
+        out = torch.empty((c.T, c.d), dtype=torch.float32, device="cuda")
+        M.moe_combine(cfg, c.T, to_dev(y_rows, torch), to_dev(slot_row, torch),
+                      to_dev(w, torch), to_dev(resid, torch) if use_res else None, out)
+        torch.cuda.synchronize()
+        want = np.einsum("tj,tjd->td", w.astype(np.float64),
+                         y_rows.astype(np.float64)[slot_row])
+        if use_res:
+            want = want + resid
+        np.testing.assert_allclose(out.cpu().numpy(), want, rtol=1e-5, atol=1e-5)
+
+
+def test_forward_residual_and_determinism():
+    c = SMALL["sig_bf16"]
+    inp, dev = inputs_of(c)
+    resid = np.random.default_rng(3).standard_normal((c.T, c.d)).astype(np.float32)
+    a, ia, ca = run_forward(c, dev, torch)
+    b, ib, cb = run_forward(c, dev, torch)
+    r, _, _ = run_forward(c, dev, torch, residual=to_dev(resid, torch))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(ia, ib) and torch.equal(ca, cb)
+    np.testing.assert_allclose(r.cpu().numpy() - a.cpu().numpy(), resid, rtol=0, atol=1e-6)
+
+
+def test_zero_router_tie_rule_on_gpu():
+    """W_r = 0 with softmax: all scores tie exactly; lower indices win."""
+    c = SMALL["soft_bf16"]
+    inp, dev = inputs_of(c)
+    dev = dict(dev, w_router=torch.zeros_like(dev["w_router"]))
+    _, idx, counts = run_forward(c, dev, torch)
+    torch.cuda.synchronize()
+    assert (idx.cpu().numpy() == np.arange(c.k)).all()
+
+
+# ------------------------------------------------------------------------ full size
+FULL_SAMPLE = {"inkling_decode": None, "inkling_prefill": 48, "qwen38": 24,
+               "inkling_skewed": 48}
+
+
+@pytest.mark.parametrize("name", list(FULL_SAMPLE))
+def test_full_size(name):
+    c = CONFIGS[name]
+    log(f"[{name}] generating inputs")
+    inp = make_inputs(c)
+    log(f"[{name}] uploading")
+    dev = device_inputs(inp, torch)
+    log(f"[{name}] forward")
+    out, idx, counts = run_forward(c, dev, torch)
+    torch.cuda.synchronize()
+    out, idx, counts = out.cpu().numpy(), idx.cpu().numpy(), counts.cpu().numpy()
+    del dev
+    torch.cuda.empty_cache()
+    log(f"[{name}] oracle routing")
+    r = O.route(c, inp["x"], inp["w_router"], inp["sel_bias"], inp["logit_offset"])
+    excl = check_routing(idx, r, c.E)
+    assert (counts[:c.E] == np.bincount(idx.ravel(), minlength=c.E)).all()
+    ns = FULL_SAMPLE[name]
+    cand = np.nonzero(~excl)[0]
+    tokens = cand if ns is None else np.sort(
+        np.random.default_rng(c.seed).choice(cand, size=ns, replace=False))
+    log(f"[{name}] oracle outputs on {len(tokens)} tokens")
+    ref = O.moe_forward(c, inp, mode="bf16_flow", tokens=tokens)
+    mx, mn = assert_outputs(out[tokens], ref.y, f"{name} forward")
+    touched = int((counts[:c.E] > 0).sum())
+    log(f"[{name}] excluded {excl.sum()}/{c.T}, touched {touched}, max count "
+        f"{counts[:c.E].max()}, max rel {mx:.2e}, mean rel {mn:.2e}")
