@@ -1,0 +1,227 @@
+"""Benchmark of the MI355X mixture-of-experts layer (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME ...]
+
+A step is one pass of the whole layer (route, group, grouped SwiGLU experts, combine)
+over one batch of seeded synthetic inputs already resident in HBM.  The headline
+workload is the Inkling-shaped prefill batch (T = 8,192), where the layer is bound by
+bf16 MFMA throughput; the Inkling-shaped decode batch (T = 32), bound by streaming the
+active experts' weights from HBM, is measured in the same run and reported in the same
+JSON line under "decode".  Rank 0 prints one JSON line.
+
+Per-stage durations come from HIP events recorded on the launch stream between the
+C-ABI calls of every timed step.  The dominant kernel work is the grouped SwiGLU step
+(m-tile plan + gate/up GEMM + down GEMM); its roofline is reported against the bf16
+MFMA peak (prefill) or the HBM peak (decode).  The CPU oracle is timed on a bounded
+token sample of the prefill workload on the host's cores as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+METRIC = ("MoE-layer tokens/s + % bf16 MFMA peak (prefill), % HBM BW (decode), 1 GPU")
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4,096 flop/clk x 2.4 GHz (dense; 2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0       # HBM3E, 8 TB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", nargs="*", default=["inkling_prefill", "inkling_decode"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=64,
+                   help="tokens of the prefill batch the oracle is timed on")
+    return p.parse_args()
+
+
+def layer_flops(c):
+    router = 2 * c.T * c.d * (c.E + c.S)
+    experts = 2 * c.T * (c.k + c.S) * 3 * c.d * c.I
+    return router, experts
+
+
+def run(c, steps, warmup, torch):
+    import numpy as np
+
+    import sparse_mixture_experts_fp32_amd as M
+    from gpu_util import cfg_struct, device_inputs
+    from moe_inputs import make_inputs
+
+    t0 = time.perf_counter()
+    inp = make_inputs(c)
+    log(f"[{c.name}] inputs generated in {time.perf_counter() - t0:.1f} s")
+    dev = device_inputs(inp, torch)
+    torch.cuda.synchronize()
+    log(f"[{c.name}] inputs resident in HBM")
+    cfg = cfg_struct(c)
+    T, A, G = c.T, c.k + c.S, c.E + c.S
+    R = T * A
+    nws = M.moe_workspace_size(cfg, T)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    idx = torch.empty((T, c.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, A), dtype=torch.float32, device="cuda")
+    counts = torch.empty((G,), dtype=torch.int32, device="cuda")
+    offsets = torch.empty((G + 1,), dtype=torch.int32, device="cuda")
+    row_token = torch.empty((R,), dtype=torch.int32, device="cuda")
+    slot_row = torch.empty((R,), dtype=torch.int32, device="cuda")
+    y_rows = torch.empty((R, c.d), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, c.d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        M.moe_route(cfg, T, dev["x"], dev["w_router"], dev.get("sel_bias"),
+                    dev.get("logit_offset"), idx, w, ws, nws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        M.moe_permute(cfg, T, idx, counts, offsets, row_token, slot_row, ws, nws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        M.moe_grouped_swiglu(cfg, T, dev["x"], offsets, row_token, dev["w_gate"],
+                             dev["w_up"], dev["w_down"], y_rows, ws, nws, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        M.moe_combine(cfg, T, y_rows, slot_row, w, None, out, stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])  # ms
+    step_ms = np.array([e[0].elapsed_time(e[4]) for e in evs])
+    cnt = counts.cpu().numpy()
+    touched = int((cnt[:c.E] > 0).sum())
+    esize = 2 if c.dtype == "bf16" else 4
+    f_router, f_experts = layer_flops(c)
+    w_bytes = (touched + c.S) * 3 * c.d * c.I * esize
+    alg_bytes = (w_bytes + (c.E + c.S) * c.d * esize + T * c.d * esize + T * c.d * 4)
+    grouped_bytes = w_bytes + T * c.d * esize + R * c.d * 4
+    ms = wall * 1e3 / steps
+    grouped_ms = float(stage[:, 2].mean())
+    res = {
+        "T": T, "ms_per_step": ms, "tokens_per_s": T * steps / wall,
+        "event_ms_per_step_median": float(np.median(step_ms)),
+        "stage_ms": {"route": float(stage[:, 0].mean()), "permute": float(stage[:, 1].mean()),
+                     "grouped_swiglu": grouped_ms, "combine": float(stage[:, 3].mean())},
+        "layer_tflops": (f_router + f_experts) / (ms * 1e-3) / 1e12,
+        "layer_alg_gbs": alg_bytes / (ms * 1e-3) / 1e9,
+        "touched_routed_experts": touched, "max_rows_per_expert": int(cnt[:c.E].max()),
+        "grouped_flops": f_experts, "grouped_alg_bytes": grouped_bytes,
+        "grouped_tflops": f_experts / (grouped_ms * 1e-3) / 1e12,
+        "grouped_gbs": grouped_bytes / (grouped_ms * 1e-3) / 1e9,
+    }
+    del dev, ws, y_rows
+    torch.cuda.empty_cache()
+    return res, inp
+
+
+def cpu_baseline(c, inp, n_tokens):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+    tokens = np.arange(min(n_tokens, c.T))
+    t0 = time.perf_counter()
+    O.moe_forward(c, inp, mode="bf16_flow", tokens=tokens)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"first {len(tokens)} tokens of the {c.name} batch (T={c.T}), "
+                      f"float64 NumPy oracle in bf16-flow mode, one call incl. routing "
+                      f"and per-expert float64 promotion"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer is built and measured on a "
+              "single MI355X (no sharding, no collectives); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from moe_inputs import CONFIGS
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    results = {}
+    prefill_inputs = None
+    for name in args.workload:
+        c = CONFIGS[name]
+        steps = args.steps if c.T >= 1024 else max(args.steps, 50)
+        res, inp = run(c, steps, args.warmup, torch)
+        results[name] = res
+        log(f"[{name}] {json.dumps(res)}")
+        if name == "inkling_prefill":
+            prefill_inputs = inp
+        else:
+            del inp
+    head = args.workload[0]
+    c = CONFIGS[head]
+    r = results[head]
+    if c.T >= 1024:
+        roof = {"bound": "mfma", "achieved": r["grouped_tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": r["grouped_tflops"] / PEAK_BF16_TFLOPS,
+                "traffic": None, "kernel": "grouped SwiGLU (gate/up + down GEMMs)"}
+    else:
+        roof = {"bound": "hbm", "achieved": r["grouped_gbs"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": r["grouped_gbs"] / PEAK_HBM_GBS, "traffic": None,
+                "kernel": "grouped SwiGLU (gate/up + down GEMMs)"}
+    line = {
+        "metric": METRIC, "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": head, "T": c.T, "d": c.d, "E": c.E, "S": c.S, "I": c.I,
+                   "k": c.k, "router": c.router},
+        "roofline": roof,
+        "layer_tflops": r["layer_tflops"],
+        "layer_frac_bf16_mfma": r["layer_tflops"] / PEAK_BF16_TFLOPS,
+        "stage_ms": r["stage_ms"],
+        "touched_routed_experts": r["touched_routed_experts"],
+    }
+    if "inkling_decode" in results and head != "inkling_decode":
+        d = results["inkling_decode"]
+        line["decode"] = {
+            "workload": "inkling_decode", "T": d["T"], "tokens_per_s": d["tokens_per_s"],
+            "ms_per_step": d["ms_per_step"], "stage_ms": d["stage_ms"],
+            "touched_routed_experts": d["touched_routed_experts"],
+            "roofline": {"bound": "hbm", "achieved": d["grouped_gbs"], "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": d["grouped_gbs"] / PEAK_HBM_GBS,
+                         "traffic": None},
+            "layer_alg_gbs": d["layer_alg_gbs"],
+            "layer_frac_hbm": d["layer_alg_gbs"] / PEAK_HBM_GBS,
+        }
+    if not args.no_cpu_baseline and prefill_inputs is not None:
+        log("timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(CONFIGS["inkling_prefill"], prefill_inputs,
+                                            args.cpu_sample)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
