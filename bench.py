@@ -43,8 +43,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", nargs="*", default=["inkling_prefill", "inkling_decode"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=64,
+    p.add_argument("--cpu-sample", type=int, default=192,
                    help="tokens of the prefill batch the oracle is timed on")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="first run one plain device-to-device copy of BYTES bytes, the "
+                        "reference kernel for scaling hardware byte counters")
     return p.parse_args()
 
 
@@ -166,6 +169,14 @@ def main():
 
     from moe_inputs import CONFIGS
     assert torch.cuda.is_available(), "bench.py needs the GPU"
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_calibration} bytes")
+        del src, dst
     results = {}
     prefill_inputs = None
     for name in args.workload:

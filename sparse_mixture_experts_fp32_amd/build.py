@@ -22,7 +22,6 @@ OBJ = os.path.join(PKG, "_build")
 HIP_SOURCES = ["router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip"]
 CXX_SOURCES = ["moe_api.cpp"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
              "-packed-fp32-ops", "-munsafe-fp-atomics"]
 
@@ -45,25 +44,28 @@ def _run(cmd):
         sys.stderr.write("\n".join(noise) + "\n")
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = True, src_dir: str = CSRC, lib: str = LIB) -> str:
+    """Compile the sources of ``src_dir`` into ``lib`` (defaults: this package's csrc/
+    into the in-tree libmoe.so)."""
+    obj_dir = OBJ if src_dir == CSRC else os.path.join(src_dir, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
     cc = hipcc()
+    flags = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{src_dir}"]
     objs = []
     for src in HIP_SOURCES:
-        o = os.path.join(OBJ, src + ".o")
-        _run([cc, *COMMON, *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", o])
+        o = os.path.join(obj_dir, src + ".o")
+        _run([cc, *flags, *HIP_FLAGS, "-x", "hip", "-c", os.path.join(src_dir, src), "-o", o])
         objs.append(o)
     for src in CXX_SOURCES:
-        o = os.path.join(OBJ, src + ".o")
-        _run([cc, *COMMON, "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, src), "-o", o])
+        o = os.path.join(obj_dir, src + ".o")
+        _run([cc, *flags, "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(src_dir, src), "-o", o])
         objs.append(o)
-    tmp = LIB + ".tmp"
-    _run([cc, "-shared", f"--offload-arch={ARCH}", "-O3", "-o", tmp,
-          *objs])
-    os.replace(tmp, LIB)
+    tmp = lib + ".tmp"
+    _run([cc, "-shared", f"--offload-arch={ARCH}", "-O3", "-o", tmp, *objs])
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

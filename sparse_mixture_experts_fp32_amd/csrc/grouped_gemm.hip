@@ -11,20 +11,19 @@
 //   down:     y[r, n] = sum_i h[r, i] Wd[n, i], f32 accumulation and f32 output.
 //
 // Work decomposition.  A device-built plan lists the m-tiles (up to 128 rows of one
-// group).  Tiles are ordered group by group, n-tile by n-tile, with the m-tiles of a
-// group fastest, so the workgroups that run together share one expert's weight slice
-// (read from HBM once, then from L2) and read the gathered rows at the same K offsets.
-// The grid is an upper bound of the tile count; workgroup ids past the real count exit,
-// and the real ones are remapped so that each XCD walks one contiguous range of tiles.
+// group).  Tiles are ordered group by group; inside a group in blocks of 4 n-tiles, m-tile
+// by m-tile, so the workgroups that run together on one XCD share a few weight slices
+// (read from HBM once, then from L2) and a few sets of gathered rows.
+// The grid is persistent (one workgroup per CU); each XCD walks one contiguous range of
+// tiles.
 //
 // Tile: 128 rows x 256 B-rows (gate/up: 128 gate + 128 up rows; down: 256 outputs).  K
 // moves 128 bytes per row per step (64 bf16 / 32 f32) through a 3-stage LDS ring filled
-// by direct global->LDS loads (global_load_lds_dwordx4), up to three steps ahead.
-// LDS rows are 128 B; 16-byte chunk c of row r sits at slot c ^ (r & 7), so the eight
-// rows read by one ds_read_b128 phase land on eight different bank groups.  A direct
-// load writes 64 lanes x 16 B contiguously, so each lane fetches the global chunk that
-// belongs at its slot.  Four waves in 2 x 2; each wave owns 64 rows x 128 B-rows as
-// 2 x 4 MFMA 32x32 tiles (128 f32 accumulators per lane).
+// by direct buffer->LDS loads (buffer_load_dwordx4 ... lds), up to three steps ahead.
+// LDS rows are 128 B; 16-byte chunk c of row r sits at slot c ^ ((r / 2) % 8).  A
+// direct load writes 64 lanes x 16 B contiguously, so each lane fetches the global chunk
+// that belongs at its slot.  Eight waves (two per SIMD, so one wave's MFMAs cover the
+// other's waits) in 2 x 4; each owns 64 rows x 64 B-rows as 2 x 2 MFMA 32x32 tiles.
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -37,18 +36,31 @@ constexpr int kStageA = kBM * kRowBytes;      // 16 KB
 constexpr int kStageB = kBRows * kRowBytes;   // 32 KB
 constexpr int kStage = kStageA + kStageB;     // 48 KB
 constexpr int kStages = 3;                    // 144 KB of the CU's 160 KB
+constexpr int kNB = 4;                        // n-tiles per scheduling block
 
+// gfx950's LDS serves a ds_read_b128 16 lanes (256 bytes, 64 banks) at a time; the
+// fragment reads of one phase touch 16 consecutive rows at one chunk.  Rows 2j and 2j+1
+// fall in different bank halves, and the XOR with (row / 2) % 8 spreads the 8 row pairs
+// over the 8 chunk slots, so one phase hits 16 distinct bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
+  return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 
-// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane.
-__device__ __forceinline__ void load_lds16(const void* g, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gbl_ptr_t)(g),
-                                   (lds_ptr_t)(lds_wave_base), 16, 0, 0);
+// Raw buffer resource over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base,
+                                                              uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
+                                           0x00020000);
+}
+
+// 16 bytes per lane from buffer offset voffset + soffset straight into LDS at
+// lds + 16 * lane (buffer_load_dwordx4 ... lds).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
+                                           uint32_t soffset, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds_wave_base), 16, voffset,
+                                           soffset, 0, 0);
 }
 
 template <typename TE>
@@ -91,8 +103,15 @@ __device__ __forceinline__ void store_h(uint16_t* p, float v) { *p = f32_to_bf16
 __device__ __forceinline__ void store_h(float* p, float v) { *p = v; }
 
 // MODE 0: gate/up + SwiGLU -> h.  MODE 1: down -> y_rows.
+//
+// Persistent: the grid has one workgroup per CU and workgroup p runs on XCD p % 8 (the
+// dispatcher deals workgroups round-robin over the XCDs).  The tiles are split into 8
+// contiguous ranges, one per XCD, and the XCD's 32 workgroups walk their range in
+// phases of 32 consecutive tiles.  Tiles take equal time, so the tiles of a phase run in
+// lockstep and the data they share (weight slices, gathered rows) is fetched into the
+// XCD's L2 once.
 template <typename TE, int MODE>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(
+__global__ __launch_bounds__(512) void grouped_gemm_kernel(
     const TE* __restrict__ a_src,           // MODE 0: x [T, K]; MODE 1: h [R, K]
     const int32_t* __restrict__ row_token,  // MODE 0 only
     const TE* __restrict__ b0,              // MODE 0: w_gate [G, N, K]; MODE 1: w_down
@@ -100,170 +119,201 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
     const int32_t* __restrict__ offsets,    // [G + 1] group row offsets
     const PlanEntry* __restrict__ plan,     // plan[0].group = m-tile count
     void* __restrict__ c_out,               // MODE 0: h [R, N] (TE); MODE 1: y [R, N] f32
+    uint32_t a_bytes,                       // bytes of a_src
     int K, int N, int T, int NT) {
   constexpr int EPC = 16 / sizeof(TE);  // elements per 16-byte chunk
-  constexpr int EPR = kRowBytes / sizeof(TE);
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage];
 
-  // ---- tile of this workgroup
   const uint32_t ntiles = static_cast<uint32_t>(plan[0].group) * NT;
-  if (blockIdx.x >= ntiles) return;
-  const uint32_t logical = xcd_remap(blockIdx.x, ntiles);
-  const PlanEntry first = plan[1 + logical / NT];
-  const int g = first.group, gmt0 = first.pad;
-  const int mg = (offsets[g + 1] - offsets[g] + kBM - 1) / kBM;  // m-tiles of the group
-  const uint32_t local = logical - static_cast<uint32_t>(gmt0) * NT;
-  const int nt = local / mg;
-  const PlanEntry pe = plan[1 + gmt0 + local % mg];
-  const int row0 = pe.row0, nrows = pe.nrows;
+  const uint32_t xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
+  const uint32_t q = ntiles / kXcds, r = ntiles % kXcds;
+  const uint32_t lo = xcd * q + (xcd < r ? xcd : r);
+  const uint32_t hi = lo + q + (xcd < r ? 1 : 0);
+
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n0 = nt * (MODE == 0 ? kGateUpBN : kDownBN);
-
-  // ---- per-lane global sources.  Wave w fills A blocks 4w..4w+3 and B blocks
-  // 8w..8w+7 (a block = 1 KB = 8 rows); lane l of a block carries row 8 b + l / 8 and
-  // logical chunk (l % 8) ^ (l / 8), which the swizzle places at physical slot l % 8.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave & 1, wn = wave >> 1;   // 2 (rows) x 4 (columns) waves
   const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;
-  uint32_t a_off[4];
+  // Lane l of LDS block b carries row 8 b + l / 8 and the logical chunk that the
+  // swizzle places at physical slot l % 8 (depends on the parity of b).
+  const int lchunk[2] = {(lane & 7) ^ ((lane >> 4) & 7),          // even blocks
+                         (lane & 7) ^ ((4 + (lane >> 4)) & 7)};   // odd blocks
+  // B-rows of this wave's two 32-wide n blocks: gate/up -> one gate block and the up
+  // block of the same h columns; down -> two adjacent output blocks.
+  int brow[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 8 * (4 * wave + i) + lrow;
-    const int rr = min(row, nrows - 1);
-    uint32_t base;
-    if (MODE == 0) {
-      int tok = row_token[row0 + rr];
-      tok = min(max(tok, 0), T - 1);
-      base = static_cast<uint32_t>(tok) * K;
-    } else {
-      base = static_cast<uint32_t>(row0 + rr) * K;
-    }
-    a_off[i] = base + lchunk * EPC;
-  }
-  // gate/up: B-rows 0..127 (waves 0, 1) are gate rows n0.., B-rows 128..255 (waves 2,
-  // 3) the up rows n0..;  down: B-rows 0..255 are w_down rows n0..
-  const TE* bsrc;
-  int brow0;
-  if (MODE == 0) {
-    bsrc = (wave < 2 ? b0 : b1) + ((size_t)g * N + n0) * K;
-    brow0 = 64 * (wave & 1);
-  } else {
-    bsrc = b0 + ((size_t)g * N + n0) * K;
-    brow0 = 64 * wave;
-  }
-  uint32_t b_off[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) b_off[i] = static_cast<uint32_t>(brow0 + 8 * i + lrow) * K +
-                                         lchunk * EPC;
-
-  const int wm = wave & 1, wn = wave >> 1;
-  int brow[4];
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
+  for (int ni = 0; ni < 2; ++ni) {
     if (MODE == 0)
-      brow[ni] = (ni < 2 ? 0 : kGateUpBN) + wn * 64 + (ni & 1) * 32 + (lane & 31);
+      brow[ni] = ni * kGateUpBN + wn * 32 + (lane & 31);
     else
-      brow[ni] = wn * 128 + ni * 32 + (lane & 31);
+      brow[ni] = wn * 64 + ni * 32 + (lane & 31);
   }
   int arow[2];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) arow[mi] = wm * 64 + mi * 32 + (lane & 31);
+  const __amdgpu_buffer_rsrc_t a_rsrc = buffer_rsrc(a_src, a_bytes);
+  const int KT = K * static_cast<int>(sizeof(TE)) / kRowBytes;
 
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x16{};
+  for (uint32_t logical = lo + blockIdx.x / kXcds; logical < hi; logical += per_xcd) {
+    // ---- the tile
+    const PlanEntry first = plan[1 + logical / NT];
+    const int g = first.group, gmt0 = first.pad;
+    const int mg = (offsets[g + 1] - offsets[g] + kBM - 1) / kBM;  // m-tiles of the group
+    // Inside a group: blocks of kNB n-tiles; within a block, m-tile by m-tile with the
+    // n-tiles fastest, so one phase covers up to 8 m-tiles x 4 n-tiles.
+    const uint32_t local = logical - static_cast<uint32_t>(gmt0) * NT;
+    const int full = NT / kNB;
+    int mloc, nt;
+    if (local < static_cast<uint32_t>(full * mg * kNB)) {
+      const int blk = local / (mg * kNB), rr = local % (mg * kNB);
+      mloc = rr / kNB;
+      nt = blk * kNB + rr % kNB;
+    } else {
+      const int rem = NT - full * kNB, rr = local - full * mg * kNB;
+      mloc = rr / rem;
+      nt = full * kNB + rr % rem;
+    }
+    const PlanEntry pe = plan[1 + gmt0 + mloc];
+    const int row0 = pe.row0, nrows = pe.nrows;
+    const int n0 = nt * (MODE == 0 ? kGateUpBN : kDownBN);
 
-  // Issue the 12 direct loads of K step kt into ring slot kt % 3.
+    // ---- per-lane sources (byte offsets).  Wave w fills A blocks 2w, 2w+1 and B blocks
+    // 4w..4w+3 of each stage (a block = 1 KB = 8 rows).
+    uint32_t a_off[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 8 * (2 * wave + i) + lrow;
+      const int rr = min(row, nrows - 1);
+      uint32_t base;
+      if (MODE == 0) {
+        int tok = row_token[row0 + rr];
+        tok = min(max(tok, 0), T - 1);
+        base = static_cast<uint32_t>(tok) * K;
+      } else {
+        base = static_cast<uint32_t>(row0 + rr) * K;
+      }
+      a_off[i] = (base + lchunk[i & 1] * EPC) * sizeof(TE);
+    }
+    // gate/up: B-rows 0..127 (waves 0..3) are gate rows n0.., B-rows 128..255 (waves
+    // 4..7) the up rows n0..;  down: B-rows 0..255 are w_down rows n0..
+    const TE* bsrc;
+    int brow0;
+    if (MODE == 0) {
+      bsrc = (wv < 4 ? b0 : b1) + ((size_t)g * N + n0) * K;
+      brow0 = 32 * (wv & 3);
+    } else {
+      bsrc = b0 + ((size_t)g * N + n0) * K;
+      brow0 = 32 * wv;
+    }
+    const __amdgpu_buffer_rsrc_t b_rsrc =
+        buffer_rsrc(bsrc, static_cast<uint32_t>((MODE == 0 ? kGateUpBN : kDownBN) * K *
+                                                sizeof(TE)));
+    uint32_t b_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      b_off[i] = (static_cast<uint32_t>(brow0 + 8 * i + lrow) * K + lchunk[i & 1] * EPC) *
+                 sizeof(TE);
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
+
+    // Issue this wave's 6 direct loads of K step kt into ring slot kt % 3.
 #define MOE_ISSUE(kt)                                                                   \
   do {                                                                                  \
     char* st_ = smem + ((kt) % kStages) * kStage;                                       \
-    const int k0_ = (kt) * EPR;                                                         \
+    const uint32_t k0_ = (kt) * kRowBytes;                                              \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
+        load_lds16(a_rsrc, a_off[i], k0_, st_ + (2 * wv + i) * 1024);                   \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                       \
-        load_lds16(a_src + a_off[i] + k0_, st_ + (4 * wave + i) * 1024);                \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                       \
-        load_lds16(bsrc + b_off[i] + k0_, st_ + kStageA + (8 * wave + i) * 1024);       \
+        load_lds16(b_rsrc, b_off[i], k0_, st_ + kStageA + (4 * wv + i) * 1024);         \
   } while (0)
 
-  // Fragments of one 16-wide (bf16) / 2-wide (f32) K step, double-buffered so the LDS
-  // reads of step s + 1 are in flight while the MFMAs of step s run.
-  typedef typename Mfma<TE>::frag_t frag_t;
-  constexpr int S = Mfma<TE>::kSteps;
-  frag_t fa[2][2], fb[2][4];
+    // Fragments of one 16-wide (bf16) / 2-wide (f32) K step, double-buffered so the LDS
+    // reads of step s + 1 are in flight while the MFMAs of step s run.
+    typedef typename Mfma<TE>::frag_t frag_t;
+    constexpr int S = Mfma<TE>::kSteps;
+    frag_t fa[2][2], fb[2][2];
 #define MOE_LOADF(st, s, buf)                                                           \
   do {                                                                                  \
     fa[buf][0] = Mfma<TE>::frag((st), arow[0], (s), lane);                              \
     fa[buf][1] = Mfma<TE>::frag((st), arow[1], (s), lane);                              \
-    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                    \
+    _Pragma("unroll") for (int ni = 0; ni < 2; ++ni)                                    \
         fb[buf][ni] = Mfma<TE>::frag((st) + kStageA, brow[ni], (s), lane);              \
   } while (0)
 
-  const int KT = K / EPR;
-  MOE_ISSUE(0);
-  if (KT > 1) MOE_ISSUE(1);
-  if (KT > 2) MOE_ISSUE(2);
-  if (KT > 2)
-    asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
-  else if (KT == 2)
-    asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  MOE_LOADF(smem, 0, 0);
-  for (int kt = 0; kt < KT; ++kt) {
-    const char* st = smem + (kt % kStages) * kStage;
+    MOE_ISSUE(0);
+    if (KT > 1) MOE_ISSUE(1);
+    if (KT > 2) MOE_ISSUE(2);
+    // s_waitcnt immediates (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+    // lgkmcnt 11:8.
+    if (KT > 2)
+      __builtin_amdgcn_s_waitcnt(0x0F7C);   // vmcnt(12)
+    else if (KT == 2)
+      __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    MOE_LOADF(smem, 0, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+      const char* st = smem + (kt % kStages) * kStage;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int cur = s & 1, nxt = cur ^ 1;
-      if (s + 1 < S) {
-        MOE_LOADF(st, s + 1, nxt);
-      } else if (kt + 1 < KT) {
-        // Stage kt + 1 must have landed (only stage kt + 2 may still be in flight) and
-        // every wave must be done reading stage kt before its slot is refilled.
-        if (kt + 2 < KT)
-          asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (kt + 3 < KT) MOE_ISSUE(kt + 3);
-        MOE_LOADF(smem + ((kt + 1) % kStages) * kStage, 0, nxt);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int s = 0; s < S; ++s) {
+        const int cur = s & 1, nxt = cur ^ 1;
+        if (s + 1 < S) {
+          MOE_LOADF(st, s + 1, nxt);
+        } else if (kt + 1 < KT) {
+          // Stage kt + 1 must have landed (only stage kt + 2 may still be in flight) and
+          // every wave must be done reading stage kt before its slot is refilled.
+          if (kt + 2 < KT)
+            __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6)
+          else
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+          // This wave's fragment reads of stage kt must be complete before any wave
+          // refills the slot (the compiler drops an lgkmcnt it does not need itself).
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          if (kt + 3 < KT) MOE_ISSUE(kt + 3);
+          MOE_LOADF(smem + ((kt + 1) % kStages) * kStage, 0, nxt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        acc[0][ni] = Mfma<TE>::mma(fa[cur][0], fb[cur][ni], acc[0][ni]);
-        acc[1][ni] = Mfma<TE>::mma(fa[cur][1], fb[cur][ni], acc[1][ni]);
+        for (int ni = 0; ni < 2; ++ni) {
+          acc[0][ni] = Mfma<TE>::mma(fa[cur][0], fb[cur][ni], acc[0][ni]);
+          acc[1][ni] = Mfma<TE>::mma(fa[cur][1], fb[cur][ni], acc[1][ni]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
-  }
 #undef MOE_LOADF
 #undef MOE_ISSUE
+    // Every wave has finished reading the ring before the next tile refills it.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // Accumulator layout of a 32x32 tile: lane l, register r -> column (l % 32),
-  // row 8 (r / 4) + 4 (l / 32) + (r % 4).
+    // Accumulator layout of a 32x32 tile: lane l, register r -> column (l % 32),
+    // row 8 (r / 4) + 4 (l / 32) + (r % 4).
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (m >= nrows) continue;
-      const size_t orow = (size_t)(row0 + m) * N;
-      if (MODE == 0) {
-        TE* h = static_cast<TE*>(c_out);
+      for (int rg = 0; rg < 16; ++rg) {
+        const int m = wm * 64 + mi * 32 + 8 * (rg >> 2) + 4 * (lane >> 5) + (rg & 3);
+        if (m >= nrows) continue;
+        const size_t orow = (size_t)(row0 + m) * N;
+        if (MODE == 0) {
+          TE* h = static_cast<TE*>(c_out);
+          const int n = n0 + wn * 32 + (lane & 31);
+          store_h(h + orow + n, silu(acc[mi][0][rg]) * acc[mi][1][rg]);
+        } else {
+          float* y = static_cast<float*>(c_out);
 #pragma unroll
-        for (int nj = 0; nj < 2; ++nj) {
-          const int n = n0 + wn * 64 + nj * 32 + (lane & 31);
-          const float gv = acc[mi][nj][r], uv = acc[mi][nj + 2][r];
-          store_h(h + orow + n, silu(gv) * uv);
-        }
-      } else {
-        float* y = static_cast<float*>(c_out);
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int n = n0 + wn * 128 + ni * 32 + (lane & 31);
-          y[orow + n] = acc[mi][ni][r];
+          for (int ni = 0; ni < 2; ++ni) {
+            const int n = n0 + wn * 64 + ni * 32 + (lane & 31);
+            y[orow + n] = acc[mi][ni][rg];
+          }
         }
       }
-    }
+  }
 }
 
 // m-tile plan: plan[0].group = number of m-tiles; plan[1 + i] = the i-th m-tile, groups in
@@ -300,15 +350,22 @@ static hipError_t launch_typed(const TE* x, const int32_t* offsets, const int32_
                                PlanEntry* plan, int T, int d, int I, int G, int R,
                                hipStream_t stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, offsets, G, plan);
-  const int64_t mtiles = max_mtiles(R, G);
+  // One workgroup per CU (the 144 KB LDS ring allows one), a multiple of the 8 XCDs.
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const uint32_t grid = static_cast<uint32_t>(cus / kXcds > 0 ? cus / kXcds * kXcds : kXcds);
   const int nt_gu = I / kGateUpBN;
-  hipLaunchKernelGGL((grouped_gemm_kernel<TE, 0>), dim3(static_cast<uint32_t>(mtiles * nt_gu)),
-                     dim3(256), 0, stream, x, row_token, wg, wu, offsets, plan,
-                     static_cast<void*>(h), d, I, T, nt_gu);
+  hipLaunchKernelGGL((grouped_gemm_kernel<TE, 0>), dim3(grid),
+                     dim3(512), 0, stream, x, row_token, wg, wu, offsets, plan,
+                     static_cast<void*>(h), static_cast<uint32_t>((size_t)T * d * sizeof(TE)),
+                     d, I, T, nt_gu);
   const int nt_dn = d / kDownBN;
-  hipLaunchKernelGGL((grouped_gemm_kernel<TE, 1>), dim3(static_cast<uint32_t>(mtiles * nt_dn)),
-                     dim3(256), 0, stream, static_cast<const TE*>(h), row_token, wd, wd,
-                     offsets, plan, static_cast<void*>(y), I, d, T, nt_dn);
+  hipLaunchKernelGGL((grouped_gemm_kernel<TE, 1>), dim3(grid),
+                     dim3(512), 0, stream, static_cast<const TE*>(h), row_token, wd, wd,
+                     offsets, plan, static_cast<void*>(y),
+                     static_cast<uint32_t>((size_t)R * I * sizeof(TE)), I, d, T, nt_dn);
   return hipGetLastError();
 }
 

@@ -58,6 +58,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m sparse_mixture_experts_fp32_amd.build`")
+    # The tensors handed to the library come from torch's HIP runtime; load that
+    # runtime first so the library binds to the same one rather than to another copy.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - torch-free use of the C ABI
+        pass
     lib = ctypes.CDLL(path)
     P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
     CFG = ctypes.POINTER(moe_config_t)
