@@ -36,6 +36,39 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+GROUPED_SOURCES = ["grouped_gemm.hip", "moe_device.h", "moe_launch.h"]
+
+
+def grouped_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GROUPED_SOURCES:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_fp32_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per launch of the grouped SwiGLU step from the committed rocprofv3 counter
+    summary of this workload, or None when the kernel sources changed since it was taken
+    (or no summary exists)."""
+    path = os.path.join(ROOT, "profiles", f"grouped_swiglu_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                fields[k.strip("`")] = v.strip().strip("`")
+    if fields.get("sources_sha256") != grouped_sources_sha256():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -60,8 +93,7 @@ def layer_flops(c):
 def run(c, steps, warmup, torch):
     import numpy as np
 
-    import sparse_mixture_experts_fp32_amd as M
-    from gpu_util import cfg_struct, device_inputs
+    from gpu_util import StagedRunner, device_inputs
     from moe_inputs import make_inputs
 
     t0 = time.perf_counter()
@@ -70,38 +102,14 @@ def run(c, steps, warmup, torch):
     dev = device_inputs(inp, torch)
     torch.cuda.synchronize()
     log(f"[{c.name}] inputs resident in HBM")
-    cfg = cfg_struct(c)
-    T, A, G = c.T, c.k + c.S, c.E + c.S
+    runner = StagedRunner(c, dev, torch)
+    T, A = c.T, c.k + c.S
     R = T * A
-    nws = M.moe_workspace_size(cfg, T)
-    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
-    idx = torch.empty((T, c.k), dtype=torch.int32, device="cuda")
-    w = torch.empty((T, A), dtype=torch.float32, device="cuda")
-    counts = torch.empty((G,), dtype=torch.int32, device="cuda")
-    offsets = torch.empty((G + 1,), dtype=torch.int32, device="cuda")
-    row_token = torch.empty((R,), dtype=torch.int32, device="cuda")
-    slot_row = torch.empty((R,), dtype=torch.int32, device="cuda")
-    y_rows = torch.empty((R, c.d), dtype=torch.float32, device="cuda")
-    out = torch.empty((T, c.d), dtype=torch.float32, device="cuda")
+    counts = runner.counts
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        M.moe_route(cfg, T, dev["x"], dev["w_router"], dev.get("sel_bias"),
-                    dev.get("logit_offset"), idx, w, ws, nws, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        M.moe_permute(cfg, T, idx, counts, offsets, row_token, slot_row, ws, nws, stream)
-        if ev is not None:
-            ev[2].record(stream)
-        M.moe_grouped_swiglu(cfg, T, dev["x"], offsets, row_token, dev["w_gate"],
-                             dev["w_up"], dev["w_down"], y_rows, ws, nws, stream)
-        if ev is not None:
-            ev[3].record(stream)
-        M.moe_combine(cfg, T, y_rows, slot_row, w, None, out, stream)
-        if ev is not None:
-            ev[4].record(stream)
+        runner.step(stream, ev)
 
     for _ in range(warmup):
         step()
@@ -136,7 +144,7 @@ def run(c, steps, warmup, torch):
         "grouped_tflops": f_experts / (grouped_ms * 1e-3) / 1e12,
         "grouped_gbs": grouped_bytes / (grouped_ms * 1e-3) / 1e9,
     }
-    del dev, ws, y_rows
+    del dev, runner
     torch.cuda.empty_cache()
     return res, inp
 
@@ -195,10 +203,12 @@ def main():
     if c.T >= 1024:
         roof = {"bound": "mfma", "achieved": r["grouped_tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": r["grouped_tflops"] / PEAK_BF16_TFLOPS,
-                "traffic": None, "kernel": "grouped SwiGLU (gate/up + down GEMMs)"}
+                "traffic": profiled_traffic(head),
+                "kernel": "grouped SwiGLU (gate/up + down GEMMs)"}
     else:
         roof = {"bound": "hbm", "achieved": r["grouped_gbs"], "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": r["grouped_gbs"] / PEAK_HBM_GBS, "traffic": None,
+                "unit": "GB/s", "frac": r["grouped_gbs"] / PEAK_HBM_GBS,
+                "traffic": profiled_traffic(head),
                 "kernel": "grouped SwiGLU (gate/up + down GEMMs)"}
     line = {
         "metric": METRIC, "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
@@ -221,7 +231,7 @@ def main():
             "touched_routed_experts": d["touched_routed_experts"],
             "roofline": {"bound": "hbm", "achieved": d["grouped_gbs"], "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": d["grouped_gbs"] / PEAK_HBM_GBS,
-                         "traffic": None},
+                         "traffic": profiled_traffic("inkling_decode")},
             "layer_alg_gbs": d["layer_alg_gbs"],
             "layer_frac_hbm": d["layer_alg_gbs"] / PEAK_HBM_GBS,
         }

@@ -12,8 +12,8 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import sparse_mixture_experts_fp32_amd as M  # noqa: E402
-from gpu_util import (cfg_struct, device_inputs, host_grouping, run_forward,  # noqa: E402
-                      to_dev, workspace)
+from gpu_util import (StagedRunner, cfg_struct, device_inputs, host_grouping,  # noqa: E402
+                      run_forward, to_dev, workspace)
 from moe_inputs import CONFIGS, MoEConfig, make_inputs  # noqa: E402
 from oracle import moe_oracle as O  # noqa: E402
 from parity import assert_outputs, check_routing, output_metrics  # noqa: E402
@@ -209,11 +209,17 @@ def test_full_size(name):
     inp = make_inputs(c)
     log(f"[{name}] uploading")
     dev = device_inputs(inp, torch)
-    log(f"[{name}] forward")
-    out, idx, counts = run_forward(c, dev, torch)
+    log(f"[{name}] staged entry points (the bench's launch sequence) and moe_forward")
+    run = StagedRunner(c, dev, torch)
+    run.step(torch.cuda.current_stream())
+    fwd, fidx, fcounts = run_forward(c, dev, torch)
     torch.cuda.synchronize()
-    out, idx, counts = out.cpu().numpy(), idx.cpu().numpy(), counts.cpu().numpy()
-    del dev
+    assert torch.equal(fwd, run.out) and torch.equal(fidx, run.idx)
+    assert torch.equal(fcounts, run.counts)
+    out, idx, counts = run.out.cpu().numpy(), run.idx.cpu().numpy(), run.counts.cpu().numpy()
+    w = run.w.cpu().numpy()
+    np.testing.assert_allclose(w.sum(1), c.route_scale, rtol=2e-6)
+    del dev, run, fwd
     torch.cuda.empty_cache()
     log(f"[{name}] oracle routing")
     r = O.route(c, inp["x"], inp["w_router"], inp["sel_bias"], inp["logit_offset"])
