@@ -18,11 +18,12 @@
 // tiles.
 //
 // Tile: 128 rows x 256 B-rows (gate/up: 128 gate + 128 up rows; down: 256 outputs).  K
-// moves 128 bytes per row per step (64 bf16 / 32 f32) through a 3-stage LDS ring filled
-// by direct buffer->LDS loads (buffer_load_dwordx4 ... lds), up to three steps ahead.
-// LDS rows are 128 B; 16-byte chunk c of row r sits at slot c ^ ((r / 2) % 8).  A
-// direct load writes 64 lanes x 16 B contiguously, so each lane fetches the global chunk
-// that belongs at its slot.  Eight waves (two per SIMD, so one wave's MFMAs cover the
+// moves 128 bytes per row per step (64 bf16 / 32 f32).  Each step is fetched from global
+// memory into registers two steps ahead (buffer_load_dwordx4), then written to one of two
+// LDS buffers with ds_write_b128; on gfx950 this outruns direct buffer->LDS loads, whose
+// LDS writes throttled the whole pipeline.  LDS rows are 128 B; 16-byte chunk c of row r
+// sits at slot c ^ ((r / 2) % 8).  A wave writes each 1 KB block as 64 lanes x 16 B, so
+// each lane fetches the global chunk that belongs at its slot.  Eight waves (two per SIMD, so one wave's MFMAs cover the
 // other's waits) in 2 x 4; each owns 64 rows x 64 B-rows as 2 x 2 MFMA 32x32 tiles.
 #include "moe_device.h"
 #include "moe_launch.h"
@@ -35,7 +36,7 @@ constexpr int kBRows = 256;
 constexpr int kStageA = kBM * kRowBytes;      // 16 KB
 constexpr int kStageB = kBRows * kRowBytes;   // 32 KB
 constexpr int kStage = kStageA + kStageB;     // 48 KB
-constexpr int kStages = 3;                    // 144 KB of the CU's 160 KB
+constexpr int kStages = 2;                    // 96 KB of the CU's 160 KB
 constexpr int kNB = 4;                        // n-tiles per scheduling block
 
 // gfx950's LDS serves a ds_read_b128 16 lanes (256 bytes, 64 banks) at a time; the
@@ -46,8 +47,6 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // Raw buffer resource over [base, base + bytes): loads past the end return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base,
                                                               uint32_t bytes) {
@@ -55,13 +54,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base,
                                            0x00020000);
 }
 
+// 16 bytes per lane from buffer offset voffset + soffset (buffer_load_dwordx4).
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
+                                        uint32_t soffset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, soffset, 0);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 // 16 bytes per lane from buffer offset voffset + soffset straight into LDS at
-// lds + 16 * lane (buffer_load_dwordx4 ... lds).
+// lds_wave_base + 16 * lane (buffer_load_dwordx4 ... lds; counted by vmcnt).
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
                                            uint32_t soffset, char* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds_wave_base), 16, voffset,
                                            soffset, 0, 0);
 }
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <typename TE>
 struct Mfma;
@@ -220,15 +231,25 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
 
-    // Issue this wave's 6 direct loads of K step kt into ring slot kt % 3.
-#define MOE_ISSUE(kt)                                                                   \
+    // Global -> registers for K step kt into register set P (6 x 16 bytes per lane), and
+    // registers -> LDS slot kt % 2.  Wave w owns 1 KB blocks of each stage; lane l writes
+    // bytes [16 l, 16 l + 16) of a block, which the swizzle maps to row 8 b + l / 8.
+    u32x4 ra[2][2], rb[2][4];
+#define MOE_FETCH(kt, P)                                                                \
   do {                                                                                  \
-    char* st_ = smem + ((kt) % kStages) * kStage;                                       \
     const uint32_t k0_ = (kt) * kRowBytes;                                              \
     _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
-        load_lds16(a_rsrc, a_off[i], k0_, st_ + (2 * wv + i) * 1024);                   \
+        ra[P][i] = load16(a_rsrc, a_off[i], k0_);                                       \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                       \
-        load_lds16(b_rsrc, b_off[i], k0_, st_ + kStageA + (4 * wv + i) * 1024);         \
+        rb[P][i] = load16(b_rsrc, b_off[i], k0_);                                       \
+  } while (0)
+#define MOE_STORE(kt, P)                                                                \
+  do {                                                                                  \
+    char* st_ = smem + ((kt) % kStages) * kStage + lane * 16;                           \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
+        *reinterpret_cast<u32x4*>(st_ + (2 * wv + i) * 1024) = ra[P][i];                \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                       \
+        *reinterpret_cast<u32x4*>(st_ + kStageA + (4 * wv + i) * 1024) = rb[P][i];      \
   } while (0)
 
     // Fragments of one 16-wide (bf16) / 2-wide (f32) K step, double-buffered so the LDS
@@ -244,50 +265,54 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
         fb[buf][ni] = Mfma<TE>::frag((st) + kStageA, brow[ni], (s), lane);              \
   } while (0)
 
-    MOE_ISSUE(0);
-    if (KT > 1) MOE_ISSUE(1);
-    if (KT > 2) MOE_ISSUE(2);
-    // s_waitcnt immediates (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt 6:4,
-    // lgkmcnt 11:8.
-    if (KT > 2)
-      __builtin_amdgcn_s_waitcnt(0x0F7C);   // vmcnt(12)
-    else if (KT == 2)
-      __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
+    // One K step kt (register set and LDS slot P = kt % 2): fetch step kt + 2 into the
+    // registers step kt vacated, run the MFMAs of step kt from LDS, and before the last
+    // MFMA group store step kt + 1 (fetched one step earlier) into the other slot.
+    // The barrier makes step kt + 1 visible and retires every read of step kt.  The
+    // fetch is unconditional (the last two steps re-fetch step KT - 1 and drop it) so
+    // that the compiler's wait before each store counts exactly the younger fetch.
+#define MOE_STEP(kt, P, NEXT)                                                           \
+  do {                                                                                  \
+    MOE_FETCH(min((kt) + 2, KT - 1), P);                                                \
+    const char* st = smem + (P) * kStage;                                               \
+    _Pragma("unroll") for (int s = 0; s < S; ++s) {                                     \
+      const int cur = s & 1, nxt = cur ^ 1;                                             \
+      if (s + 1 < S) {                                                                  \
+        MOE_LOADF(st, s + 1, nxt);                                                      \
+      } else if (NEXT) {                                                                \
+        MOE_STORE((kt) + 1, (P) ^ 1);                                                   \
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                 \
+        MOE_LOADF(smem + ((P) ^ 1) * kStage, 0, nxt);                                   \
+      }                                                                                 \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      _Pragma("unroll") for (int ni = 0; ni < 2; ++ni) {                                \
+        acc[0][ni] = Mfma<TE>::mma(fa[cur][0], fb[cur][ni], acc[0][ni]);                \
+        acc[1][ni] = Mfma<TE>::mma(fa[cur][1], fb[cur][ni], acc[1][ni]);                \
+      }                                                                                 \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+    }                                                                                   \
+  } while (0)
+
+    // KT is even: d and I are multiples of 256 and 128 elements, i.e. of 2 K steps.  The
+    // last step (NEXT = 0) is peeled off the loop so that no control-flow join sits
+    // between a fragment load and the MFMAs that do not depend on it (the waitcnt pass
+    // would wait for every outstanding load at a join).
+    MOE_FETCH(0, 0);
+    MOE_FETCH(1, 1);
+    MOE_STORE(0, 0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     MOE_LOADF(smem, 0, 0);
-    for (int kt = 0; kt < KT; ++kt) {
-      const char* st = smem + (kt % kStages) * kStage;
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const int cur = s & 1, nxt = cur ^ 1;
-        if (s + 1 < S) {
-          MOE_LOADF(st, s + 1, nxt);
-        } else if (kt + 1 < KT) {
-          // Stage kt + 1 must have landed (only stage kt + 2 may still be in flight) and
-          // every wave must be done reading stage kt before its slot is refilled.
-          if (kt + 2 < KT)
-            __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6)
-          else
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-          // This wave's fragment reads of stage kt must be complete before any wave
-          // refills the slot (the compiler drops an lgkmcnt it does not need itself).
-          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-          if (kt + 3 < KT) MOE_ISSUE(kt + 3);
-          MOE_LOADF(smem + ((kt + 1) % kStages) * kStage, 0, nxt);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          acc[0][ni] = Mfma<TE>::mma(fa[cur][0], fb[cur][ni], acc[0][ni]);
-          acc[1][ni] = Mfma<TE>::mma(fa[cur][1], fb[cur][ni], acc[1][ni]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    int kt = 0;
+    for (; kt + 2 < KT; kt += 2) {
+      MOE_STEP(kt, 0, 1);
+      MOE_STEP(kt + 1, 1, 1);
     }
+    MOE_STEP(kt, 0, 1);
+    MOE_STEP(kt + 1, 1, 0);
+#undef MOE_STEP
 #undef MOE_LOADF
-#undef MOE_ISSUE
+#undef MOE_STORE
+#undef MOE_FETCH
     // Every wave has finished reading the ring before the next tile refills it.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
@@ -316,16 +341,307 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
   }
 }
 
+// ---- 256 x 256 tiles (bf16 layers whose groups average at least 128 rows)
+//
+// Same decomposition and plan as above with 256-row m-tiles.  A 256 x 256 tile moves
+// 64 KB per 64-wide K step for 2 x 256 x 256 x 64 flops, two thirds of the bytes per
+// flop of the 128 x 256 tile, so the CU's vector-memory path and the L2 keep up with
+// the MFMAs.  The K step is split into two halves, the 256 B-rows (32 KB) and the 256
+// A rows (32 KB), streamed by direct buffer->LDS loads through a ring of 5 half slots
+// (160 KB): half h (even: B of step h / 2, odd: A of step h / 2) goes to slot h % 5.
+// While step kt runs, halves 2kt + 2 .. 2kt + 4 are in flight; the barrier that ends
+// step kt frees the slots of halves 2kt and 2kt + 1, which take halves 2kt + 5 and
+// 2kt + 6.  The weight halves are issued two steps before use, the row halves one.
+// Eight waves in 2 (rows) x 4 (B-rows); each owns 128 rows x 64 B-rows as 4 x 2 MFMA
+// 32x32 tiles.  Waves 0..3 hold rows 0..127 and waves 4..7 rows 128..255, one of each
+// per SIMD, so a group's last m-tile with at most 128 rows costs each SIMD half a tile:
+// waves 4..7 then only take part in the loads and barriers.
+constexpr int kWBM = 256;
+constexpr int kWHalf = 256 * kRowBytes;   // 32 KB
+constexpr int kWSlots = 5;                // 160 KB, the whole LDS of a CU
+constexpr bool kPhaseSync = true;
+constexpr int kWLoadWaves = 4;            // waves that issue the loads (4 or 8)
+constexpr int kWNB = 32 / kWLoadWaves;    // 1 KB blocks per loader wave per half
+constexpr int kSpinLimit = 4000;          // polls of a phase wait (~1.5 ms at most)
+
+template <int MODE>
+__global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
+    const uint16_t* __restrict__ a_src,      // MODE 0: x [T, K]; MODE 1: h [R, K]
+    const int32_t* __restrict__ row_token,   // MODE 0 only
+    const uint16_t* __restrict__ b0,         // MODE 0: w_gate [G, N, K]; MODE 1: w_down
+    const uint16_t* __restrict__ b1,         // MODE 0: w_up [G, N, K]
+    const int32_t* __restrict__ offsets,     // [G + 1] group row offsets
+    const PlanEntry* __restrict__ plan,      // 256-row m-tiles; plan[0].group = count
+    uint32_t* __restrict__ sync,             // [8] phase counters, zero at launch
+    void* __restrict__ c_out,                // MODE 0: h [R, N] bf16; MODE 1: y [R, N] f32
+    uint32_t a_bytes, int K, int N, int T, int NT) {
+  typedef uint16_t TE;
+  constexpr int EPC = 8;  // bf16 elements per 16-byte chunk
+  __shared__ __attribute__((aligned(1024))) char smem[kWSlots * kWHalf];
+
+  const uint32_t ntiles = static_cast<uint32_t>(plan[0].group) * NT;
+  const uint32_t xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
+  const uint32_t q = ntiles / kXcds, r = ntiles % kXcds;
+  const uint32_t lo = xcd * q + (xcd < r ? xcd : r);
+  const uint32_t hi = lo + q + (xcd < r ? 1 : 0);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wv >> 2, wn = wv & 3;
+  const int lrow = lane >> 3;
+  const int lchunk[2] = {(lane & 7) ^ ((lane >> 4) & 7),
+                         (lane & 7) ^ ((4 + (lane >> 4)) & 7)};
+  int brow[2];
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) {
+    if (MODE == 0)
+      brow[ni] = ni * kGateUpBN + wn * 32 + (lane & 31);
+    else
+      brow[ni] = wn * 64 + ni * 32 + (lane & 31);
+  }
+  int arow[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) arow[mi] = wm * 128 + mi * 32 + (lane & 31);
+  const __amdgpu_buffer_rsrc_t a_rsrc = buffer_rsrc(a_src, a_bytes);
+  const int KT = K * static_cast<int>(sizeof(TE)) / kRowBytes;
+  const int H = 2 * KT;
+
+  uint32_t phase = 0;
+  for (uint32_t logical = lo + blockIdx.x / kXcds; logical < hi;
+       logical += per_xcd, ++phase) {
+    if (kPhaseSync) {
+      // The XCD's workgroups start each phase together, so the tiles of a phase stay
+      // within a few K steps of each other and share their weight and row halves
+      // through the L2.  Phases 0..p hold min(32 (p + 1), hi - lo) tiles.  The wait is
+      // bounded: a workgroup that waits kSpinLimit polls goes on alone.
+      if (tid == 0) {
+        __hip_atomic_fetch_add(sync + xcd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t target = min((phase + 1) * per_xcd, hi - lo);
+        for (int it = 0; it < kSpinLimit; ++it) {
+          if (__hip_atomic_load(sync + xcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+              target)
+            break;
+          __builtin_amdgcn_s_sleep(4);
+        }
+      }
+      asm volatile("s_barrier" ::: "memory");
+    }
+    const PlanEntry first = plan[1 + logical / NT];
+    const int g = first.group, gmt0 = first.pad;
+    const int mg = (offsets[g + 1] - offsets[g] + kWBM - 1) / kWBM;
+    const uint32_t local = logical - static_cast<uint32_t>(gmt0) * NT;
+    const int full = NT / kNB;
+    int mloc, nt;
+    if (local < static_cast<uint32_t>(full * mg * kNB)) {
+      const int blk = local / (mg * kNB), rr = local % (mg * kNB);
+      mloc = rr / kNB;
+      nt = blk * kNB + rr % kNB;
+    } else {
+      const int rem = NT - full * kNB, rr = local - full * mg * kNB;
+      mloc = rr / rem;
+      nt = full * kNB + rr % rem;
+    }
+    const PlanEntry pe = plan[1 + gmt0 + mloc];
+    const int row0 = pe.row0, nrows = pe.nrows;
+    const int n0 = nt * (MODE == 0 ? kGateUpBN : kDownBN);
+    const bool active = wm * 128 < nrows;   // wave-uniform
+
+    // The kWLoadWaves waves wv >= 8 - kWLoadWaves issue every load: loader lw fills 1 KB
+    // blocks kWNB lw .. kWNB lw + kWNB - 1 (rows / B-rows 8 kWNB lw ..) of every half.
+    const bool loader = wv >= 8 - kWLoadWaves;   // wave-uniform
+    const int lw = loader ? wv - (8 - kWLoadWaves) : 0;
+    uint32_t a_off[kWNB];
+#pragma unroll
+    for (int i = 0; i < kWNB; ++i) {
+      const int row = 8 * kWNB * lw + 8 * i + lrow;
+      const int rr = min(row, nrows - 1);
+      uint32_t base;
+      if (MODE == 0) {
+        int tok = row_token[row0 + rr];
+        tok = min(max(tok, 0), T - 1);
+        base = static_cast<uint32_t>(tok) * K;
+      } else {
+        base = static_cast<uint32_t>(row0 + rr) * K;
+      }
+      a_off[i] = (base + lchunk[i & 1] * EPC) * sizeof(TE);
+    }
+    // gate/up: B-rows 0..127 are gate rows n0.., 128..255 the up rows n0..;  down: B-rows
+    // 0..255 are w_down rows n0..  Block i of a loader is B-row brow0 + 8 i + lane / 8.
+    const TE* bsrc;
+    int brow0;
+    if (MODE == 0) {
+      bsrc = (lw < kWLoadWaves / 2 ? b0 : b1) + ((size_t)g * N + n0) * K;
+      brow0 = 8 * kWNB * (lw % (kWLoadWaves / 2));
+    } else {
+      bsrc = b0 + ((size_t)g * N + n0) * K;
+      brow0 = 8 * kWNB * lw;
+    }
+    const __amdgpu_buffer_rsrc_t b_rsrc =
+        buffer_rsrc(bsrc, static_cast<uint32_t>((MODE == 0 ? kGateUpBN : kDownBN) * K *
+                                                sizeof(TE)));
+    // Blocks 2j + p sit 16 j rows below blocks p: a per-lane base per parity plus a
+    // uniform offset.
+    uint32_t b_base[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      b_base[p] = (static_cast<uint32_t>(brow0 + 8 * p + lrow) * K + lchunk[p] * EPC) *
+                  sizeof(TE);
+    const uint32_t b_pair = 16u * K * sizeof(TE);
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
+
+    // Loads i0 .. i0 + kWNB / 2 - 1 of this wave's kWNB blocks of the A half of step k
+    // (slot (2k + 1) % 5) or of the B half of step k (slot 2k % 5); loader waves only.
+#define MOE_WLOAD_A(k, i0)                                                              \
+  do {                                                                                  \
+    if (loader) {                                                                       \
+      char* st_ = smem + ((2 * (k) + 1) % kWSlots) * kWHalf + lw * (kWNB * 1024);       \
+      _Pragma("unroll") for (int i = (i0); i < (i0) + kWNB / 2; ++i)                    \
+          load_lds16(a_rsrc, a_off[i], (k) * kRowBytes, st_ + i * 1024);                \
+    }                                                                                   \
+  } while (0)
+#define MOE_WLOAD_B(k, i0)                                                              \
+  do {                                                                                  \
+    if (loader) {                                                                       \
+      char* st_ = smem + ((2 * (k)) % kWSlots) * kWHalf + lw * (kWNB * 1024);           \
+      _Pragma("unroll") for (int i = (i0); i < (i0) + kWNB / 2; ++i)                    \
+          load_lds16(b_rsrc, b_base[i & 1], (k) * kRowBytes + (i >> 1) * b_pair,        \
+                     st_ + i * 1024);                                                   \
+    }                                                                                   \
+  } while (0)
+
+    bf16x8 fa[2][4], fb[2][2];
+#define MOE_WLOADF(sa, sb, s, buf)                                                      \
+  do {                                                                                  \
+    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                    \
+        fa[buf][mi] = Mfma<TE>::frag((sa), arow[mi], (s), lane);                        \
+    _Pragma("unroll") for (int ni = 0; ni < 2; ++ni)                                    \
+        fb[buf][ni] = Mfma<TE>::frag((sb), brow[ni], (s), lane);                        \
+  } while (0)
+
+    // Halves 0, 1, 2 (B and A of step 0, B of step 1); wait for halves 0 and 1.  During
+    // step kt the wave issues halves 2kt + 3 (A of step kt + 1, two loads in each of
+    // substeps 0 and 1) and 2kt + 4 (B of step kt + 2, substeps 2 and 3), into the slots
+    // that the barrier ending step kt - 1 freed; spreading them over the step keeps the
+    // L1's miss queue busy without stalling a wave's MFMA issue on a burst of loads.
+    MOE_WLOAD_B(0, 0);
+    MOE_WLOAD_B(0, kWNB / 2);
+    MOE_WLOAD_A(0, 0);
+    MOE_WLOAD_A(0, kWNB / 2);
+    MOE_WLOAD_B(1, 0);
+    MOE_WLOAD_B(1, kWNB / 2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWNB));
+    asm volatile("s_barrier" ::: "memory");
+
+    if (active) {
+      // MFMAs of substep s from fragment buffer s % 2; substeps 0..2 first load the
+      // fragments of substep s + 1 into the other buffer.  The last two K steps are
+      // peeled off the loop so that no control-flow join sits between a fragment load
+      // and the MFMAs that do not depend on it (the waitcnt pass would wait for every
+      // load at a join).
+#define MOE_WMMA(cur)                                                                   \
+  do {                                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                    \
+        _Pragma("unroll") for (int ni = 0; ni < 2; ++ni)                                \
+            acc[mi][ni] = Mfma<TE>::mma(fa[cur][mi], fb[cur][ni], acc[mi][ni]);         \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+  } while (0)
+      // Step kt; ISSA / ISSB: issue A of step kt + 1 / B of step kt + 2; NEXT: a step
+      // follows (wait, barrier, first fragments of step kt + 1).
+#define MOE_WSTEP(kt, ISSA, ISSB, NEXT)                                                 \
+  do {                                                                                  \
+    const char* sa_ = smem + ((2 * (kt) + 1) % kWSlots) * kWHalf;                       \
+    const char* sb_ = smem + ((2 * (kt)) % kWSlots) * kWHalf;                           \
+    if (ISSA) MOE_WLOAD_A((kt) + 1, 0);                                                 \
+    MOE_WLOADF(sa_, sb_, 1, 1);                                                         \
+    MOE_WMMA(0);                                                                        \
+    if (ISSA) MOE_WLOAD_A((kt) + 1, kWNB / 2);                                          \
+    MOE_WLOADF(sa_, sb_, 2, 0);                                                         \
+    MOE_WMMA(1);                                                                        \
+    if (ISSB) MOE_WLOAD_B((kt) + 2, 0);                                                 \
+    MOE_WLOADF(sa_, sb_, 3, 1);                                                         \
+    MOE_WMMA(0);                                                                        \
+    if (ISSB) MOE_WLOAD_B((kt) + 2, kWNB / 2);                                          \
+    if (NEXT) {                                                                         \
+      /* Halves 2kt + 2 and 2kt + 3 (step kt + 1) must have landed; only half 2kt + 4 \
+         may still be in flight. */                                                     \
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((ISSB) ? kWNB : 0));                         \
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                   \
+      MOE_WLOADF(smem + ((2 * (kt) + 3) % kWSlots) * kWHalf,                            \
+                 smem + ((2 * (kt) + 2) % kWSlots) * kWHalf, 0, 0);                     \
+    }                                                                                   \
+    MOE_WMMA(1);                                                                        \
+  } while (0)
+      MOE_WLOADF(smem + kWHalf, smem, 0, 0);
+      int kt = 0;
+      for (; kt + 2 < KT; ++kt) MOE_WSTEP(kt, 1, 1, 1);
+      MOE_WSTEP(kt, 1, 0, 1);
+      MOE_WSTEP(kt + 1, 0, 0, 0);
+#undef MOE_WSTEP
+#undef MOE_WMMA
+    } else {
+      // No rows for this wave in this tile: the same loads, waits and barriers.
+      for (int kt = 0; kt + 1 < KT; ++kt) {
+        MOE_WLOAD_A(kt + 1, 0);
+        MOE_WLOAD_A(kt + 1, kWNB / 2);
+        if (kt + 2 < KT) {
+          MOE_WLOAD_B(kt + 2, 0);
+          MOE_WLOAD_B(kt + 2, kWNB / 2);
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWNB));
+        } else {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    }
+#undef MOE_WLOADF
+#undef MOE_WLOAD_B
+#undef MOE_WLOAD_A
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    if (active) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) {
+          const int m = wm * 128 + mi * 32 + 8 * (rg >> 2) + 4 * (lane >> 5) + (rg & 3);
+          if (m >= nrows) continue;
+          const size_t orow = (size_t)(row0 + m) * N;
+          if (MODE == 0) {
+            TE* h = static_cast<TE*>(c_out);
+            const int n = n0 + wn * 32 + (lane & 31);
+            store_h(h + orow + n, silu(acc[mi][0][rg]) * acc[mi][1][rg]);
+          } else {
+            float* y = static_cast<float*>(c_out);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+              const int n = n0 + wn * 64 + ni * 32 + (lane & 31);
+              y[orow + n] = acc[mi][ni][rg];
+            }
+          }
+        }
+    }
+  }
+}
+
 // m-tile plan: plan[0].group = number of m-tiles; plan[1 + i] = the i-th m-tile, groups in
-// order, 128 rows each except a group's last; .pad holds the group's first m-tile.
+// order, BM rows each except a group's last; .pad holds the group's first m-tile.
+template <int BM>
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets,
-                                                    int G, PlanEntry* __restrict__ plan) {
+                                                    int G, PlanEntry* __restrict__ plan,
+                                                    uint32_t* __restrict__ sync) {
   __shared__ int32_t scan[1024];
   const int g = threadIdx.x;
+  if (g < 4 * kSyncEntries) sync[g] = 0;
   int c = 0, m = 0;
   if (g < G) {
     c = offsets[g + 1] - offsets[g];
-    m = (c + kBM - 1) / kBM;
+    m = (c + BM - 1) / BM;
   }
   scan[g] = m;
   __syncthreads();
@@ -340,7 +656,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (g < G) {
     const int r0 = offsets[g];
     for (int i = 0; i < m; ++i)
-      plan[1 + start + i] = PlanEntry{g, r0 + i * kBM, min(kBM, c - i * kBM), start};
+      plan[1 + start + i] = PlanEntry{g, r0 + i * BM, min(BM, c - i * BM), start};
   }
 }
 
@@ -349,19 +665,39 @@ static hipError_t launch_typed(const TE* x, const int32_t* offsets, const int32_
                                const TE* wg, const TE* wu, const TE* wd, TE* h, float* y,
                                PlanEntry* plan, int T, int d, int I, int G, int R,
                                hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, offsets, G, plan);
-  // One workgroup per CU (the 144 KB LDS ring allows one), a multiple of the 8 XCDs.
+  // One workgroup per CU (the LDS ring allows one), a multiple of the 8 XCDs.
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   const uint32_t grid = static_cast<uint32_t>(cus / kXcds > 0 ? cus / kXcds * kXcds : kXcds);
   const int nt_gu = I / kGateUpBN;
+  const int nt_dn = d / kDownBN;
+  uint32_t* sync = reinterpret_cast<uint32_t*>(plan + 1 + max_mtiles(R, G));
+  if (sizeof(TE) == 2 && static_cast<int64_t>(R) >= static_cast<int64_t>(kWBM / 2) * G) {
+    // Groups average at least 128 rows: 256-row tiles.
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+    hipLaunchKernelGGL(plan_kernel<kWBM>, dim3(1), dim3(1024), 0, stream, offsets, G, plan,
+                       sync);
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<0>), dim3(grid), dim3(512), 0, stream, xb,
+                       row_token, reinterpret_cast<const uint16_t*>(wg),
+                       reinterpret_cast<const uint16_t*>(wu), offsets, plan, sync,
+                       static_cast<void*>(h), static_cast<uint32_t>((size_t)T * d * 2), d, I,
+                       T, nt_gu);
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<1>), dim3(grid), dim3(512), 0, stream,
+                       reinterpret_cast<const uint16_t*>(h), row_token,
+                       reinterpret_cast<const uint16_t*>(wd),
+                       reinterpret_cast<const uint16_t*>(wd), offsets, plan, sync + kXcds,
+                       static_cast<void*>(y), static_cast<uint32_t>((size_t)R * I * 2), I, d,
+                       T, nt_dn);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(plan_kernel<kBM>, dim3(1), dim3(1024), 0, stream, offsets, G, plan,
+                     sync);
   hipLaunchKernelGGL((grouped_gemm_kernel<TE, 0>), dim3(grid),
                      dim3(512), 0, stream, x, row_token, wg, wu, offsets, plan,
                      static_cast<void*>(h), static_cast<uint32_t>((size_t)T * d * sizeof(TE)),
                      d, I, T, nt_gu);
-  const int nt_dn = d / kDownBN;
   hipLaunchKernelGGL((grouped_gemm_kernel<TE, 1>), dim3(grid),
                      dim3(512), 0, stream, static_cast<const TE*>(h), row_token, wd, wd,
                      offsets, plan, static_cast<void*>(y),

@@ -50,4 +50,9 @@ hipError_t launch_combine(const float* y_rows, const int32_t* slot_row, const fl
 // Upper bound of the grouped GEMM's m-tiles for R rows in G groups.
 inline int64_t max_mtiles(int64_t R, int64_t G) { return R / kGemmBM + G; }
 
+// The plan buffer: entry 0 (m-tile count), the m-tiles, then kSyncEntries entries that
+// hold 16 uint32 phase counters (8 XCDs x 2 GEMMs), cleared by the plan kernel.
+constexpr int kSyncEntries = 4;
+inline int64_t plan_entries(int64_t R, int64_t G) { return 1 + max_mtiles(R, G) + kSyncEntries; }
+
 }  // namespace moe

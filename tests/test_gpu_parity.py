@@ -47,6 +47,13 @@ SMALL = {c.name: c for c in [
           seed=16),
     small("sig_bf16_logit_bias", "sigmoid", "bf16", T=200, d=512, E=48, S=2, I=128, k=6,
           seed=17).with_(bias_on_logits=True),
+    # bf16 layers whose groups average >= 128 rows take 256-row tiles: groups of one to
+    # three m-tiles with tails above and below 128 rows, K of 2 to 16 steps.
+    small("sig_bf16_wide", "sigmoid", "bf16", T=600, d=1024, E=12, S=2, I=512, k=2, seed=18),
+    small("sig_bf16_wide_short_k", "sigmoid", "bf16", T=512, d=256, E=4, S=1, I=128, k=2,
+          seed=20),
+    # Several n-tiles and m-tiles with ragged tails in f32.
+    small("soft_f32_wide", "softmax", "f32", T=150, d=512, E=6, S=0, I=256, k=2, seed=19),
 ]}
 
 _cache = {}
