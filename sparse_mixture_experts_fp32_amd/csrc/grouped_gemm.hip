@@ -131,7 +131,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
     const PlanEntry* __restrict__ plan,     // plan[0].group = m-tile count
     void* __restrict__ c_out,               // MODE 0: h [R, N] (TE); MODE 1: y [R, N] f32
     uint32_t a_bytes,                       // bytes of a_src
-    int K, int N, int T, int NT) {
+    int K, int N, int T, int NT,
+    int lda, int ldc) {                     // row pitch (elements) of a_src and c_out
   constexpr int EPC = 16 / sizeof(TE);  // elements per 16-byte chunk
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage];
 
@@ -199,9 +200,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
       if (MODE == 0) {
         int tok = row_token[row0 + rr];
         tok = min(max(tok, 0), T - 1);
-        base = static_cast<uint32_t>(tok) * K;
+        base = static_cast<uint32_t>(tok) * lda;
       } else {
-        base = static_cast<uint32_t>(row0 + rr) * K;
+        base = static_cast<uint32_t>(row0 + rr) * lda;
       }
       a_off[i] = (base + lchunk[i & 1] * EPC) * sizeof(TE);
     }
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
       for (int rg = 0; rg < 16; ++rg) {
         const int m = wm * 64 + mi * 32 + 8 * (rg >> 2) + 4 * (lane >> 5) + (rg & 3);
         if (m >= nrows) continue;
-        const size_t orow = (size_t)(row0 + m) * N;
+        const size_t orow = (size_t)(row0 + m) * ldc;
         if (MODE == 0) {
           TE* h = static_cast<TE*>(c_out);
           const int n = n0 + wn * 32 + (lane & 31);
@@ -374,7 +375,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
     const PlanEntry* __restrict__ plan,      // 256-row m-tiles; plan[0].group = count
     uint32_t* __restrict__ sync,             // [8] phase counters, zero at launch
     void* __restrict__ c_out,                // MODE 0: h [R, N] bf16; MODE 1: y [R, N] f32
-    uint32_t a_bytes, int K, int N, int T, int NT) {
+    uint32_t a_bytes, int K, int N, int T, int NT,
+    int lda, int ldc) {                      // row pitch (elements) of a_src and c_out
   typedef uint16_t TE;
   constexpr int EPC = 8;  // bf16 elements per 16-byte chunk
   __shared__ __attribute__((aligned(1024))) char smem[kWSlots * kWHalf];
@@ -409,11 +411,13 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
   uint32_t phase = 0;
   for (uint32_t logical = lo + blockIdx.x / kXcds; logical < hi;
        logical += per_xcd, ++phase) {
-    if (kPhaseSync) {
+    if (kPhaseSync && MODE == 0) {
       // The XCD's workgroups start each phase together, so the tiles of a phase stay
       // within a few K steps of each other and share their weight and row halves
       // through the L2.  Phases 0..p hold min(32 (p + 1), hi - lo) tiles.  The wait is
-      // bounded: a workgroup that waits kSpinLimit polls goes on alone.
+      // bounded: a workgroup that waits kSpinLimit polls goes on alone.  (Measured on
+      // the Inkling prefill shape: faster for gate/up, slower for the shorter down
+      // tiles, which run unsynchronized.)
       if (tid == 0) {
         __hip_atomic_fetch_add(sync + xcd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t target = min((phase + 1) * per_xcd, hi - lo);
@@ -459,9 +463,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
       if (MODE == 0) {
         int tok = row_token[row0 + rr];
         tok = min(max(tok, 0), T - 1);
-        base = static_cast<uint32_t>(tok) * K;
+        base = static_cast<uint32_t>(tok) * lda;
       } else {
-        base = static_cast<uint32_t>(row0 + rr) * K;
+        base = static_cast<uint32_t>(row0 + rr) * lda;
       }
       a_off[i] = (base + lchunk[i & 1] * EPC) * sizeof(TE);
     }
@@ -611,7 +615,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
         for (int rg = 0; rg < 16; ++rg) {
           const int m = wm * 128 + mi * 32 + 8 * (rg >> 2) + 4 * (lane >> 5) + (rg & 3);
           if (m >= nrows) continue;
-          const size_t orow = (size_t)(row0 + m) * N;
+          const size_t orow = (size_t)(row0 + m) * ldc;
           if (MODE == 0) {
             TE* h = static_cast<TE*>(c_out);
             const int n = n0 + wn * 32 + (lane & 31);
@@ -674,7 +678,8 @@ static hipError_t launch_typed(const TE* x, const int32_t* offsets, const int32_
   const int nt_gu = I / kGateUpBN;
   const int nt_dn = d / kDownBN;
   uint32_t* sync = reinterpret_cast<uint32_t*>(plan + 1 + max_mtiles(R, G));
-  if (sizeof(TE) == 2 && static_cast<int64_t>(R) >= static_cast<int64_t>(kWBM / 2) * G) {
+  const int hp = static_cast<int>(h_pitch(I));
+  if (sizeof(TE) == 2 && use_wide_tiles(1, R, G)) {
     // Groups average at least 128 rows: 256-row tiles.
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
     hipLaunchKernelGGL(plan_kernel<kWBM>, dim3(1), dim3(1024), 0, stream, offsets, G, plan,
@@ -683,13 +688,13 @@ static hipError_t launch_typed(const TE* x, const int32_t* offsets, const int32_
                        row_token, reinterpret_cast<const uint16_t*>(wg),
                        reinterpret_cast<const uint16_t*>(wu), offsets, plan, sync,
                        static_cast<void*>(h), static_cast<uint32_t>((size_t)T * d * 2), d, I,
-                       T, nt_gu);
+                       T, nt_gu, d, hp);
     hipLaunchKernelGGL((grouped_gemm_wide_kernel<1>), dim3(grid), dim3(512), 0, stream,
                        reinterpret_cast<const uint16_t*>(h), row_token,
                        reinterpret_cast<const uint16_t*>(wd),
                        reinterpret_cast<const uint16_t*>(wd), offsets, plan, sync + kXcds,
-                       static_cast<void*>(y), static_cast<uint32_t>((size_t)R * I * 2), I, d,
-                       T, nt_dn);
+                       static_cast<void*>(y), static_cast<uint32_t>((size_t)R * hp * 2), I, d,
+                       T, nt_dn, hp, d);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(plan_kernel<kBM>, dim3(1), dim3(1024), 0, stream, offsets, G, plan,
@@ -697,11 +702,12 @@ static hipError_t launch_typed(const TE* x, const int32_t* offsets, const int32_
   hipLaunchKernelGGL((grouped_gemm_kernel<TE, 0>), dim3(grid),
                      dim3(512), 0, stream, x, row_token, wg, wu, offsets, plan,
                      static_cast<void*>(h), static_cast<uint32_t>((size_t)T * d * sizeof(TE)),
-                     d, I, T, nt_gu);
+                     d, I, T, nt_gu, d, hp);
   hipLaunchKernelGGL((grouped_gemm_kernel<TE, 1>), dim3(grid),
                      dim3(512), 0, stream, static_cast<const TE*>(h), row_token, wd, wd,
                      offsets, plan, static_cast<void*>(y),
-                     static_cast<uint32_t>((size_t)R * I * sizeof(TE)), I, d, T, nt_dn);
+                     static_cast<uint32_t>((size_t)R * hp * sizeof(TE)), I, d, T, nt_dn, hp,
+                     d);
   return hipGetLastError();
 }
 

@@ -78,7 +78,7 @@ Layout layout_of(const moe_config_t& c, int64_t T) {
   L.slot_row = take(sizeof(int32_t) * m.R);
   L.hist = take(sizeof(int32_t) * nb * m.E);
   L.plan = take(sizeof(PlanEntry) * moe::plan_entries(m.R, m.G));
-  L.h = take(esize * m.R * m.I);
+  L.h = take(esize * m.R * moe::h_pitch(m.I));
   L.y = take(sizeof(float) * m.R * m.d);
   L.total = off;
   return L;

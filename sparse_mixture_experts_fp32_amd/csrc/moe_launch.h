@@ -35,7 +35,8 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int S, int k,
                           int32_t* block_hist, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* slot_row, hipStream_t stream);
 
-// Grouped gate/up (+SwiGLU) and down GEMMs.  h is [R, I] (dtype), y_rows [R, d] f32.
+// Grouped gate/up (+SwiGLU) and down GEMMs.  h is [R, I] (dtype) with row pitch
+// h_pitch(I), y_rows [R, d] f32.
 hipError_t launch_grouped_swiglu(int dtype, const void* x, const int32_t* offsets,
                                  const int32_t* row_token, const void* w_gate,
                                  const void* w_up, const void* w_down, void* h,
@@ -49,6 +50,16 @@ hipError_t launch_combine(const float* y_rows, const int32_t* slot_row, const fl
 
 // Upper bound of the grouped GEMM's m-tiles for R rows in G groups.
 inline int64_t max_mtiles(int64_t R, int64_t G) { return R / kGemmBM + G; }
+
+// Row pitch (elements) of the intermediate h [R, I]: 64 elements of padding per row, so
+// that the rows one K step of a tile reads do not all share their low address bits.
+constexpr int kHPad = 64;
+inline int64_t h_pitch(int64_t I) { return I + kHPad; }
+
+// bf16 layers whose groups average at least 128 rows run the 256-row tiling.
+inline bool use_wide_tiles(int dtype, int64_t R, int64_t G) {
+  return dtype == 1 && R >= 128 * G;
+}
 
 // The plan buffer: entry 0 (m-tile count), the m-tiles, then kSyncEntries entries that
 // hold 16 uint32 phase counters (8 XCDs x 2 GEMMs), cleared by the plan kernel.
