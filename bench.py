@@ -76,7 +76,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", nargs="*", default=["inkling_prefill", "inkling_decode"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=192,
+    p.add_argument("--cpu-sample", type=int, default=512,
                    help="tokens of the prefill batch the oracle is timed on")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="first run one plain device-to-device copy of BYTES bytes, the "
