@@ -59,7 +59,8 @@ typedef enum {
 } moe_status_t;
 
 typedef enum {
-  MOE_ROUTER_SOFTMAX_TOPK = 0,    /* softmax over E, top-k, renormalize (S must be 0) */
+  MOE_ROUTER_SOFTMAX_TOPK = 0,    /* softmax over E, top-k, renormalize; S ungated shared
+                                     experts (weight 1, no router rows) */
   MOE_ROUTER_SIGMOID_SHARED = 1   /* sigmoid over E + S, bias-steered top-k, joint norm */
 } moe_router_t;
 
@@ -70,7 +71,7 @@ typedef struct {
   int32_t n_experts;       /* E: routed experts */
   int32_t d_ff;            /* I: expert intermediate size */
   int32_t top_k;           /* k: routed experts per token */
-  int32_t n_shared;        /* S: shared (always-active) experts; 0 for softmax */
+  int32_t n_shared;        /* S: shared (always-active) experts, 0..8 */
   int32_t router;          /* moe_router_t */
   int32_t dtype;           /* moe_dtype_t of x, w_router and the expert weights */
   int32_t bias_on_logits;  /* sigmoid router: 0 = selection bias added to the score
@@ -86,17 +87,20 @@ const char* moe_status_str(moe_status_t status);
  * never touches the GPU).  The same workspace serves all entry points. */
 moe_status_t moe_workspace_size(const moe_config_t* cfg, int64_t T, size_t* bytes);
 
-/* Router: logits over the E + S experts with f32 accumulation of exact products,
- * selection, and combine weights (definition: the router row of the component table of
- * "Qwen3.8-2.4T-A95B vs Inkling"; shared-expert weighting: "Inkling vs Gemma 4 31B",
- * shared-expert row).
- *   x [T, d] (dtype), w_router [E + S, d] (dtype)
+/* Router: logits with f32 accumulation of exact products, selection, and combine
+ * weights (definition: the router row of the component table of "Qwen3.8-2.4T-A95B vs
+ * Inkling"; shared-expert weighting: "Inkling vs Gemma 4 31B", shared-expert row, which
+ * sets Inkling's router-weighted shared experts against the blueprint's ungated one).
+ *   x [T, d] (dtype)
+ *   w_router [NR, d] (dtype): sigmoid router NR = E + S (shared experts' rows last);
+ *            softmax router NR = E (its shared experts are ungated and have no row)
  *   sel_bias [E] f32 or NULL: sigmoid router only; steers selection, not the weights
  *   logit_offset [E] f32 or NULL: added to the routed experts' logits before scoring
  *   topk_idx [T, k] int32 out: routed experts in descending selection score; equal
  *            scores keep the lower index first
  *   weights  [T, k + S] f32 out: the routed experts' weights in topk_idx order, then the
- *            shared experts' weights; they sum to route_scale (sigmoid) or 1 (softmax)
+ *            shared experts' weights; sigmoid: all k + S sum to route_scale; softmax: the
+ *            k routed weights sum to 1 and each shared weight is exactly 1
  *   ws: workspace of at least moe_workspace_size() bytes. */
 moe_status_t moe_route(const moe_config_t* cfg, int64_t T, const void* x,
                        const void* w_router, const float* sel_bias,

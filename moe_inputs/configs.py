@@ -45,6 +45,12 @@ class MoEConfig:
         return float(self.k + self.S) if self.router == "sigmoid" else 1.0
 
     @property
+    def router_rows(self) -> int:
+        """Rows of the router weight: E + S for the sigmoid router (shared experts score
+        too); E for the softmax router, whose shared experts are ungated."""
+        return self.E + self.S if self.router == "sigmoid" else self.E
+
+    @property
     def n_active(self) -> int:
         return self.k + self.S
 
@@ -73,6 +79,11 @@ CONFIGS: dict[str, MoEConfig] = {
     "qwen38": MoEConfig(name="qwen38", T=4096, d=8192, E=512, S=0, I=2048, k=10,
                         router="softmax", dtype="bf16", x_std=1.0, w_std=0.02,
                         bias_std=0.0, zipf_s=0.0, zipf_hot_share=0.0, seed=3),
+    # Qwen3.8-shaped layer with its ungated shared expert (I = 2,048, weight 1).
+    "qwen38_shared": MoEConfig(name="qwen38_shared", T=4096, d=8192, E=512, S=1, I=2048,
+                               k=10, router="softmax", dtype="bf16", x_std=1.0,
+                               w_std=0.02, bias_std=0.0, zipf_s=0.0, zipf_hot_share=0.0,
+                               seed=5),
     # Inkling shape with a Zipf(1.2) per-expert logit offset: ~30% of assignments on
     # the 8 hottest experts.
     "inkling_skewed": MoEConfig(name="inkling_skewed", T=16384, seed=4,
@@ -81,3 +92,5 @@ CONFIGS: dict[str, MoEConfig] = {
 
 # The order in which the five workloads are listed everywhere.
 CONFIG_ORDER = ["tiny_fp32", "inkling_decode", "inkling_prefill", "qwen38", "inkling_skewed"]
+# Workloads beyond the five above: Qwen3.8 with its ungated shared expert.
+EXTRA_ORDER = ["qwen38_shared"]

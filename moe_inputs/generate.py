@@ -12,7 +12,8 @@ holds none of the layer's arithmetic.  It only draws numbers:
 
 Layouts (row-major, contiguous):
   x          [T, d]
-  w_router   [E + S, d]   (shared experts' rows last)
+  w_router   [NR, d]      (sigmoid: NR = E + S, shared experts' rows last; softmax:
+                           NR = E, its shared experts are ungated)
   sel_bias   [E]          (sigmoid router only)
   logit_off  [E]          (Zipf-skewed workload only)
   w_gate     [E + S, I, d]
@@ -92,7 +93,8 @@ def make_x(cfg: MoEConfig, T: int | None = None) -> np.ndarray:
 
 
 def make_w_router(cfg: MoEConfig) -> np.ndarray:
-    return _draw(_rng(cfg.seed, "w_router", 0), (cfg.E + cfg.S, cfg.d), cfg.w_std, cfg.dtype)
+    return _draw(_rng(cfg.seed, "w_router", 0), (cfg.router_rows, cfg.d), cfg.w_std,
+                 cfg.dtype)
 
 
 def make_sel_bias(cfg: MoEConfig) -> np.ndarray | None:

@@ -18,6 +18,13 @@ What the layer computes (all citations are to the pages' component tables):
       count (same row, Inkling column); each shared expert "is weighted by its own router
       score, normalized jointly with the routed scores" (Inkling vs Gemma 4 31B, component
       table, shared-expert row).
+* Shared experts of the softmax router.  In the blueprint, one or two shared experts
+  run on every token (Qwen3.5-397B-A17B vs Inkling, block diagram, shared-expert box),
+  and the blueprint's shared expert carries no gate, unlike Inkling's router-weighted
+  ones (Inkling vs Gemma 4 31B, component table, shared-expert row).  Qwen3.8 keeps one
+  of intermediate size 2,048 (Qwen3.8 2.4T A95B atlas page, raw config
+  shared_expert_intermediate_size).  Reading: its output is added with weight 1, outside
+  the renormalized routed mixture, and it has no router row.
 * Experts.  SwiGLU FFNs: E(x) = W_down (SiLU(W_gate x) * W_up x), SiLU(z) = z / (1 + e^-z)
   (Inkling vs Gemma 4 31B, routed-expert and shared-expert rows; Qwen3.8 2.4T A95B atlas
   page, key facts "Activation silu" and raw config hidden_act).
@@ -30,6 +37,7 @@ Readings where the pages leave a step open (each is listed in the design notes):
     other reading, bias added to the logit, is a flag;
   - the bias steers selection only; weights use the raw sigmoid scores;
   - shared experts' scores are the sigmoid of their own router rows (last S rows);
+  - the softmax router's shared experts are ungated: weight exactly 1, no router row;
   - the "x8" constant is the active count k + S (``route_scale``);
   - ties in selection go to the lower expert index;
   - bf16 workloads ("bf16-flow" mode) round the SwiGLU intermediate h to bf16 once,
@@ -116,7 +124,7 @@ class Routing:
     gap: np.ndarray      # [T] k-th minus (k+1)-th selection score
     sel: np.ndarray      # [T, E] selection scores (sigmoid: s + b; softmax: p)
     scores: np.ndarray   # [T, E + S] sigmoid scores s, or [T, E] softmax probabilities p
-    logits: np.ndarray   # [T, E + S]
+    logits: np.ndarray   # [T, E + S] (sigmoid) or [T, E] (softmax)
     counts: np.ndarray   # [E] tokens routed to each routed expert
 
 
@@ -146,17 +154,20 @@ def route_sigmoid_shared(logits: np.ndarray, E: int, S: int, k: int, route_scale
     return Routing(idx, w, gap, sel, s, logits, counts)
 
 
-def route_softmax_topk(logits: np.ndarray, E: int, k: int,
+def route_softmax_topk(logits: np.ndarray, E: int, k: int, S: int = 0,
                        forced_idx: np.ndarray | None = None) -> Routing:
     """Softmax top-k router (Qwen3.8-2.4T-A95B vs Inkling, component table, router row,
     Qwen3.8 column): p = softmax(l) over the E routed experts, keep the k largest,
-    renormalize: w_j = p_j / sum_topk p.  No selection bias."""
+    renormalize: w_j = p_j / sum_topk p.  No selection bias.  The S shared experts are
+    ungated (the blueprint's shared expert; Inkling vs Gemma 4 31B, shared-expert row):
+    weight 1 each, after the k routed weights."""
     p = softmax(logits[:, :E])
     idx, gap = top_k_descending(p, k)
     if forced_idx is not None:
         idx = np.asarray(forced_idx, dtype=np.int64)
     pa = np.take_along_axis(p, idx, axis=1)
     w = pa / pa.sum(axis=1, keepdims=True)
+    w = np.concatenate([w, np.ones((w.shape[0], S))], axis=1)
     counts = np.bincount(idx.ravel(), minlength=E)
     return Routing(idx, w, gap, p, p, logits, counts)
 
@@ -171,8 +182,8 @@ def route(cfg, x, w_router, sel_bias=None, logit_offset=None, tokens=None,
     if cfg.router == "sigmoid":
         return route_sigmoid_shared(l, cfg.E, cfg.S, cfg.k, cfg.route_scale, sel_bias,
                                     cfg.bias_on_logits, forced_idx)
-    assert cfg.router == "softmax" and cfg.S == 0
-    return route_softmax_topk(l, cfg.E, cfg.k, forced_idx)
+    assert cfg.router == "softmax"
+    return route_softmax_topk(l, cfg.E, cfg.k, cfg.S, forced_idx)
 
 
 # ----------------------------------------------------------------------------- experts

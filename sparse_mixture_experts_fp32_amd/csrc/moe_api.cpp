@@ -26,6 +26,7 @@ struct Layout {
 
 struct Dims {
   int64_t T, d, E, S, I, k, A, G, R;
+  int64_t NR;  // router rows: E + S (sigmoid) or E (softmax: ungated shared experts)
 };
 
 Dims dims_of(const moe_config_t& c, int64_t T) {
@@ -39,13 +40,14 @@ Dims dims_of(const moe_config_t& c, int64_t T) {
   m.A = m.k + m.S;
   m.G = m.E + m.S;
   m.R = T * m.A;
+  m.NR = c.router == MOE_ROUTER_SIGMOID_SHARED ? m.G : m.E;
   return m;
 }
 
 // Router K split: enough workgroups to cover the chip at small T, chunks of >= 256.
 void router_split(const Dims& m, int* nsplit, int* kchunk) {
   const int64_t tiles = ((m.T + moe::kRouterTile - 1) / moe::kRouterTile) *
-                        ((m.G + moe::kRouterTile - 1) / moe::kRouterTile);
+                        ((m.NR + moe::kRouterTile - 1) / moe::kRouterTile);
   int64_t maxsplit = m.d / 256 > 0 ? m.d / 256 : 1;
   int64_t want = tiles > 0 ? (512 + tiles - 1) / tiles : 1;
   int64_t ns = want < maxsplit ? want : maxsplit;
@@ -69,7 +71,7 @@ Layout layout_of(const moe_config_t& c, int64_t T) {
     off += align_up(bytes);
     return at;
   };
-  L.part = take(sizeof(float) * L.nsplit * m.T * m.G);
+  L.part = take(sizeof(float) * L.nsplit * m.T * m.NR);
   L.idx = take(sizeof(int32_t) * m.T * m.k);
   L.wts = take(sizeof(float) * m.T * m.A);
   L.counts = take(sizeof(int32_t) * m.G);
@@ -96,7 +98,7 @@ moe_status_t check_cfg(const moe_config_t* c) {
   if (c->top_k > c->n_experts) return MOE_ERR_ARG;
   if (!std::isfinite(c->route_scale) || !(c->route_scale > 0.0f)) return MOE_ERR_ARG;
   if (c->router == MOE_ROUTER_SOFTMAX_TOPK &&
-      (c->n_shared != 0 || c->route_scale != 1.0f || c->bias_on_logits != 0))
+      (c->route_scale != 1.0f || c->bias_on_logits != 0))
     return MOE_ERR_ARG;
   if (c->top_k > 32 || c->n_shared > 8 || c->n_experts + c->n_shared > 1024)
     return MOE_ERR_UNSUPPORTED;
@@ -153,7 +155,7 @@ moe_status_t do_route(const moe_config_t& c, int64_t T, const void* x, const voi
   const Dims m = dims_of(c, T);
   float* part = at<float>(ws, L.part);
   MOE_TRY(finish(moe::launch_router_logits(c.dtype, x, w_router, part, (int)m.T, (int)m.d,
-                                           (int)m.G, L.nsplit, L.kchunk, stream),
+                                           (int)m.NR, L.nsplit, L.kchunk, stream),
                  stream));
   return finish(moe::launch_topk(part, L.nsplit, (int)m.T, (int)m.E, (int)m.S, (int)m.k,
                                  c.router, c.bias_on_logits, c.route_scale, sel_bias,

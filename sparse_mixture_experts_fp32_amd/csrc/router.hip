@@ -135,9 +135,10 @@ hipError_t launch_router_logits(int dtype, const void* x, const void* w_router, 
 //   sigmoid: s = 1 / (1 + exp(-l)); selection score s + b (or sigmoid(l + b) when the
 //            bias applies to the logit); weight route_scale * s_j / sum over the active
 //            set (routed in selection order, then shared) of s.
-//   softmax: selection on the logit (monotone in the probability); weight
-//            exp(l_j - l_top) / sum over the top k of exp(l_i - l_top), which equals the
-//            renormalized softmax probability.
+//   softmax: logits over the E routed experts only; selection on the logit (monotone
+//            in the probability); weight exp(l_j - l_top) / sum over the top k of
+//            exp(l_i - l_top), which equals the renormalized softmax probability; the S
+//            shared experts are ungated: weight 1.
 // ---------------------------------------------------------------------------------------
 template <int MAXV>
 __global__ __launch_bounds__(256) void topk_kernel(
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
   __shared__ float sden[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
-  const int NE = E + S;
+  const int NE = router == 1 ? E + S : E;   // logit columns
   const bool live = t < T;
   float raw[MAXV];
   uint64_t key[MAXV];
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
       for (int j = 0; j < A; ++j) den += sval[wave][j];
     } else {
       const float top = sval[wave][0];
-      for (int j = 0; j < A; ++j) den += expf(sval[wave][j] - top);
+      for (int j = 0; j < k; ++j) den += expf(sval[wave][j] - top);
     }
     sden[wave] = den;
   }
@@ -218,7 +219,8 @@ __global__ __launch_bounds__(256) void topk_kernel(
   if (live && lane < A) {
     const float den = sden[wave];
     const float v = sval[wave][lane];
-    const float w = (router == 1) ? route_scale * v / den : expf(v - sval[wave][0]) / den;
+    const float w = (router == 1) ? route_scale * v / den
+                    : (lane < k ? expf(v - sval[wave][0]) / den : 1.0f);
     weights[(size_t)t * A + lane] = w;
   }
 }
@@ -227,7 +229,7 @@ hipError_t launch_topk(const float* part, int nsplit, int T, int E, int S, int k
                        int bias_on_logits, float route_scale, const float* sel_bias,
                        const float* logit_offset, int32_t* topk_idx, float* weights,
                        hipStream_t stream) {
-  const int per_lane = (E + S + 63) / 64;
+  const int per_lane = ((router == 1 ? E + S : E) + 63) / 64;
   dim3 grid((T + 3) / 4);
 #define MOE_TOPK(MV)                                                                      \
   hipLaunchKernelGGL(topk_kernel<MV>, grid, dim3(256), 0, stream, part, nsplit, T, E, S, \

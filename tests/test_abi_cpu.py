@@ -71,13 +71,18 @@ def test_config_validation(bad, status):
     assert ei.value.status == status
 
 
-def test_softmax_router_rejects_shared_experts_and_scale():
+def test_softmax_router_takes_ungated_shared_experts_but_no_scale():
     c = CONFIGS["qwen38"]
+    # Ungated shared experts are accepted (up to 8); they add T rows each.
+    base = M.moe_workspace_size(cfg_of(c), 8)
+    assert M.moe_workspace_size(cfg_of(c, n_shared=1), 8) > base
     with pytest.raises(M.MoEError) as ei:
-        M.moe_workspace_size(cfg_of(c, n_shared=1), 8)
-    assert ei.value.status == M.MOE_ERR_ARG
+        M.moe_workspace_size(cfg_of(c, n_shared=9), 8)
+    assert ei.value.status == M.MOE_ERR_UNSUPPORTED
     with pytest.raises(M.MoEError):
         M.moe_workspace_size(cfg_of(c, route_scale=2.0), 8)
+    with pytest.raises(M.MoEError):
+        M.moe_workspace_size(cfg_of(c, bias_on_logits=True), 8)
 
 
 def test_entry_points_validate_before_launch():

@@ -27,6 +27,8 @@ def log(*a):
 
 
 def small(name, router, dtype, T, d, E, S, I, k, w_std=0.05, seed=10, bias_std=0.1):
+    """Small parity shape.  The softmax router gets shared experts only through
+    ``small_shared`` (ungated)."""
     sig = router == "sigmoid"
     return MoEConfig(name=name, T=T, d=d, E=E, S=S if sig else 0, I=I, k=k, router=router,
                      dtype=dtype, x_std=1.0, w_std=w_std, bias_std=bias_std if sig else 0.0,
@@ -54,6 +56,13 @@ SMALL = {c.name: c for c in [
           seed=20),
     # Several n-tiles and m-tiles with ragged tails in f32.
     small("soft_f32_wide", "softmax", "f32", T=150, d=512, E=6, S=0, I=256, k=2, seed=19),
+    # Softmax router with ungated shared experts (weight 1, no router row), both tilings.
+    small("soft_bf16_shared", "softmax", "bf16", T=257, d=512, E=32, S=0, I=256, k=4,
+          seed=21).with_(S=1),
+    small("soft_f32_shared", "softmax", "f32", T=100, d=256, E=16, S=0, I=128, k=2,
+          seed=22).with_(S=2),
+    small("soft_bf16_shared_wide", "softmax", "bf16", T=700, d=256, E=4, S=0, I=256, k=2,
+          seed=23).with_(S=1),
 ]}
 
 _cache = {}
@@ -102,7 +111,12 @@ def test_route_stage(name):
     excl = check_routing(idx, r, c.E)
     ok = ~excl
     # Weights follow the selection order; compare where the sets agree.
-    np.testing.assert_allclose(w.sum(1), c.route_scale, rtol=2e-6)
+    # sigmoid: all k + S weights sum to route_scale; softmax: the routed ones to 1, and
+    # each ungated shared weight is 1.
+    np.testing.assert_allclose(w.sum(1), c.route_scale if c.router == "sigmoid"
+                               else 1.0 + c.S, rtol=2e-6)
+    if c.router == "softmax" and c.S:
+        assert (w[:, c.k:] == 1.0).all()
     same_order = (idx == r.idx).all(1) & ok
     np.testing.assert_allclose(w[same_order], r.weights[same_order], rtol=2e-5, atol=0)
 
@@ -206,7 +220,7 @@ def test_zero_router_tie_rule_on_gpu():
 
 # ------------------------------------------------------------------------ full size
 FULL_SAMPLE = {"inkling_decode": None, "inkling_prefill": 48, "qwen38": 24,
-               "inkling_skewed": 48}
+               "inkling_skewed": 48, "qwen38_shared": 24}
 
 
 @pytest.mark.parametrize("name", list(FULL_SAMPLE))
@@ -225,7 +239,12 @@ def test_full_size(name):
     assert torch.equal(fcounts, run.counts)
     out, idx, counts = run.out.cpu().numpy(), run.idx.cpu().numpy(), run.counts.cpu().numpy()
     w = run.w.cpu().numpy()
-    np.testing.assert_allclose(w.sum(1), c.route_scale, rtol=2e-6)
+    # sigmoid: all k + S weights sum to route_scale; softmax: the routed ones to 1, and
+    # each ungated shared weight is 1.
+    np.testing.assert_allclose(w.sum(1), c.route_scale if c.router == "sigmoid"
+                               else 1.0 + c.S, rtol=2e-6)
+    if c.router == "softmax" and c.S:
+        assert (w[:, c.k:] == 1.0).all()
     del dev, run, fwd
     torch.cuda.empty_cache()
     log(f"[{name}] oracle routing")

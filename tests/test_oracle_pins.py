@@ -84,6 +84,22 @@ def test_worked_example_softmax_topk():
                                atol=1e-7)
 
 
+def test_worked_example_softmax_ungated_shared():
+    """tests/golden/worked_examples.md, Example C."""
+    ln3, ln7 = math.log(3), math.log(7)
+    cfg = MoEConfig(name="wC", T=1, d=4, E=3, S=1, I=4, k=2, router="softmax", dtype="f32",
+                    x_std=1, w_std=1, bias_std=0, zipf_s=0, zipf_hot_share=0, seed=0)
+    experts = [(ln3, 1, 1, 1), (1, 1, 1, 3), (ln7, 2, 1, 2), (-ln3, 1, 2, 0)]
+    inp = worked_inputs(3, 1, [ln3, 0, math.log(2), 0], None, experts)
+    inp["w_router"] = inp["w_router"][:3]          # the shared expert has no router row
+    out = O.moe_forward(cfg, inp, mode="exact")
+    assert out.routing.idx.tolist() == [[0, 2]]
+    np.testing.assert_allclose(out.routing.gap, [1 / 6], rtol=1e-6)
+    np.testing.assert_allclose(out.routing.weights, [[3 / 5, 2 / 5, 1]], rtol=1e-6)
+    np.testing.assert_allclose(out.y, [[-0.5 * ln3, 0.45 * ln3, 0.7 * ln7, 0]], rtol=1e-6,
+                               atol=1e-7)
+
+
 # ---------------------------------------------------------------- numbers
 def test_promote_bf16_bit_patterns():
     bits = np.array([0x3F80, 0xC000, 0x0001, 0x7F7F, 0x0000, 0x8000, 0x3F81], np.uint16)
@@ -256,7 +272,8 @@ def per_token_reference(cfg, inp, round_h):
     E, S, k = cfg.E, cfg.S, cfg.k
     ys, idxs, ws = [], [], []
     for t in range(cfg.T):
-        logits = [sum(x[t, c] * wr[e, c] for c in range(cfg.d)) for e in range(E + S)]
+        logits = [sum(x[t, c] * wr[e, c] for c in range(cfg.d))
+                  for e in range(cfg.router_rows)]
         if cfg.router == "sigmoid":
             s = [1 / (1 + math.exp(-v)) for v in logits]
             sel = [s[e] + float(b[e]) for e in range(E)]
@@ -270,9 +287,10 @@ def per_token_reference(cfg, inp, round_h):
             z = sum(ex)
             p = [v / z for v in ex]
             chosen = sorted(range(E), key=lambda e: (-p[e], e))[:k]
-            act = chosen
-            tot = sum(p[e] for e in act)
-            w = [p[e] / tot for e in act]
+            tot = sum(p[e] for e in chosen)
+            # ungated shared experts: weight 1 each, outside the renormalization
+            act = chosen + list(range(E, E + S))
+            w = [p[e] / tot for e in chosen] + [1.0] * S
         y = [0.0] * cfg.d
         for wj, e in zip(w, act):
             wg, wu, wd = f(inp["w_gate"][e]), f(inp["w_up"][e]), f(inp["w_down"][e])
@@ -301,6 +319,44 @@ def test_oracle_matches_per_token_loop(router, dtype):
     assert (out.routing.idx == idx).all()
     np.testing.assert_allclose(out.routing.weights, w, rtol=1e-12)
     np.testing.assert_allclose(out.y, y, rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_oracle_matches_per_token_loop_softmax_shared(dtype):
+    cfg = MoEConfig(name="soft_shared", T=6, d=8, E=6, S=2, I=5, k=2, router="softmax",
+                    dtype=dtype, x_std=1.0, w_std=0.3, bias_std=0.0, zipf_s=0.0,
+                    zipf_hot_share=0.0, seed=13)
+    inp = make_inputs(cfg)
+    assert inp["w_router"].shape == (cfg.E, cfg.d)
+    mode = "bf16_flow" if dtype == "bf16" else "exact"
+    out = O.moe_forward(cfg, inp, mode=mode)
+    y, idx, w = per_token_reference(cfg, inp, round_h=(dtype == "bf16"))
+    assert (out.routing.idx == idx).all()
+    np.testing.assert_allclose(out.routing.weights, w, rtol=1e-12)
+    np.testing.assert_allclose(out.y, y, rtol=1e-9, atol=1e-12)
+
+
+def test_ungated_shared_expert_adds_its_dense_output():
+    """With the shared experts the softmax layer's output is the routed-only output (the
+    same routing) plus, for every token, the plain sum of the shared experts' SwiGLU
+    outputs: nothing renormalizes them and no score scales them."""
+    cfg = MoEConfig(name="soft_shared2", T=16, d=16, E=8, S=2, I=12, k=3, router="softmax",
+                    dtype="f32", x_std=1.0, w_std=0.3, bias_std=0.0, zipf_s=0.0,
+                    zipf_hot_share=0.0, seed=14)
+    inp = make_inputs(cfg)
+    with_shared = O.moe_forward(cfg, inp, mode="exact")
+    routed_only = O.moe_forward(cfg.with_(S=0), inp, mode="exact")
+    assert (with_shared.routing.idx == routed_only.routing.idx).all()
+    np.testing.assert_allclose(with_shared.routing.weights[:, :cfg.k],
+                               routed_only.routing.weights, rtol=1e-15)
+    x = inp["x"].astype(np.float64)
+    dense = np.zeros_like(with_shared.y)
+    for s in range(cfg.S):
+        e = cfg.E + s
+        g = x @ inp["w_gate"][e].astype(np.float64).T
+        u = x @ inp["w_up"][e].astype(np.float64).T
+        dense += (g * u / (1 + np.exp(-g))) @ inp["w_down"][e].astype(np.float64).T
+    np.testing.assert_allclose(with_shared.y - routed_only.y, dense, rtol=1e-9, atol=1e-12)
 
 
 def test_bf16_flow_differs_from_exact_at_the_single_rounding_point():
