@@ -153,6 +153,29 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x,
                          int32_t* topk_idx_out, int32_t* counts_out, void* ws,
                          size_t ws_bytes, hipStream_t stream);
 
+/* Pre-norm RMSNorm of the layer input, the step that pre-norm blocks run before the
+ * layer ("Qwen3.5-397B-A17B vs Inkling" and "Qwen3.8-2.4T-A95B vs Inkling", residual-stream
+ * rows and block diagrams; zero-centred gains for Qwen3.8; rms_norm_eps on the Qwen3.8
+ * atlas page):
+ *   y[t, c] = x[t, c] / sqrt(mean_c x[t, c]^2 + eps) * (zero_centred + gain[c])
+ * with the sum of squares accumulated in f32; bf16 layers round y once to bf16 (nearest
+ * even).  x, y [T, d] and gain [d] in the config's dtype; eps > 0; zero_centred 0 or 1.
+ * d <= 16384 (MOE_ERR_UNSUPPORTED above).  y may not alias x. */
+moe_status_t moe_rmsnorm(const moe_config_t* cfg, int64_t T, const void* x,
+                         const void* gain, float eps, int32_t zero_centred, void* y,
+                         hipStream_t stream);
+
+/* The pre-norm block's branch in one call: moe_rmsnorm of the raw hidden states x into the
+ * workspace, then moe_forward on the normalized input.  Arguments as in moe_rmsnorm and
+ * moe_forward (the residual, if given, is added to the layer's output). */
+moe_status_t moe_forward_rmsnorm(const moe_config_t* cfg, int64_t T, const void* x,
+                                 const void* norm_gain, float eps, int32_t zero_centred,
+                                 const void* w_router, const float* sel_bias,
+                                 const float* logit_offset, const void* w_gate,
+                                 const void* w_up, const void* w_down, const float* residual,
+                                 float* out, int32_t* topk_idx_out, int32_t* counts_out,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -5,5 +5,5 @@ the layer itself."""
 from .configs import CONFIGS, CONFIG_ORDER, EXTRA_ORDER, MoEConfig  # noqa: F401
 from .generate import (  # noqa: F401
     EXPERT_TENSORS, f32_to_bf16_bits, fill_expert_tensor, make_expert, make_inputs,
-    make_logit_offset, make_sel_bias, make_w_router, make_x, storage_dtype,
+    make_logit_offset, make_norm_gain, make_sel_bias, make_w_router, make_x, storage_dtype,
 )

@@ -37,6 +37,9 @@ class MoEConfig:
     zipf_hot_share: float  # target share of assignments on the 8 hottest experts
     seed: int
     bias_on_logits: bool = False  # selection bias on the score (False) or on the logit
+    prenorm: bool = False         # x is the raw hidden state; the layer input is RMSNorm(x)
+    norm_zero_centred: bool = False  # RMSNorm scale is 1 + g (stored g) instead of g
+    norm_eps: float = 1e-6
 
     @property
     def route_scale(self) -> float:
@@ -88,9 +91,17 @@ CONFIGS: dict[str, MoEConfig] = {
     # the 8 hottest experts.
     "inkling_skewed": MoEConfig(name="inkling_skewed", T=16384, seed=4,
                                 **{**_INKLING, "zipf_s": 1.2, "zipf_hot_share": 0.30}),
+    # Kimi K3-style latent experts: sigmoid 16-of-896 in a 3,584-wide latent, RMSNorm
+    # before the experts' up-projection (plain gains); I = 3,072 is a reading (the pages
+    # give none; 2.8T parameters over 93 layers of 896 x 3 x 3,584 x I suggest ~3,100).
+    "kimi_k3_latent": MoEConfig(name="kimi_k3_latent", T=8192, d=3584, E=896, S=0, I=3072,
+                                k=16, router="sigmoid", dtype="bf16", x_std=1.0,
+                                w_std=0.02, bias_std=0.1, zipf_s=0.0, zipf_hot_share=0.0,
+                                seed=6, prenorm=True),
 }
 
 # The order in which the five workloads are listed everywhere.
 CONFIG_ORDER = ["tiny_fp32", "inkling_decode", "inkling_prefill", "qwen38", "inkling_skewed"]
-# Workloads beyond the five above: Qwen3.8 with its ungated shared expert.
-EXTRA_ORDER = ["qwen38_shared"]
+# Workloads beyond the five above: Qwen3.8 with its ungated shared expert; Kimi K3-style
+# latent experts behind a pre-norm RMSNorm.
+EXTRA_ORDER = ["qwen38_shared", "kimi_k3_latent"]

@@ -16,6 +16,7 @@ Layouts (row-major, contiguous):
                            NR = E, its shared experts are ungated)
   sel_bias   [E]          (sigmoid router only)
   logit_off  [E]          (Zipf-skewed workload only)
+  norm_gain  [d]          (pre-norm workloads only; RMSNorm gains in the layer dtype)
   w_gate     [E + S, I, d]
   w_up       [E + S, I, d]
   w_down     [E + S, d, I]
@@ -31,7 +32,7 @@ import numpy as np
 from .configs import MoEConfig
 
 TENSOR_IDS = {"x": 1, "w_router": 2, "sel_bias": 3, "zipf_rank": 4,
-              "w_gate": 5, "w_up": 6, "w_down": 7}
+              "w_gate": 5, "w_up": 6, "w_down": 7, "norm_gain": 8}
 X_BLOCK = 1024  # tokens per x stream
 _CALIB_FILE = os.path.join(os.path.dirname(__file__), "zipf_calibration.json")
 
@@ -95,6 +96,17 @@ def make_x(cfg: MoEConfig, T: int | None = None) -> np.ndarray:
 def make_w_router(cfg: MoEConfig) -> np.ndarray:
     return _draw(_rng(cfg.seed, "w_router", 0), (cfg.router_rows, cfg.d), cfg.w_std,
                  cfg.dtype)
+
+
+def make_norm_gain(cfg: MoEConfig) -> np.ndarray | None:
+    """RMSNorm gains [d] in the layer dtype for pre-norm workloads: stored g ~ N(0, 0.1^2)
+    for zero-centred gains (scale 1 + g), 1 + N(0, 0.1^2) for plain gains."""
+    if not cfg.prenorm:
+        return None
+    g = _rng(cfg.seed, "norm_gain", 0).standard_normal(cfg.d, dtype=np.float32) * 0.1
+    if not cfg.norm_zero_centred:
+        g = g + np.float32(1.0)
+    return f32_to_bf16_bits(g) if cfg.dtype == "bf16" else g.astype(np.float32)
 
 
 def make_sel_bias(cfg: MoEConfig) -> np.ndarray | None:
@@ -164,6 +176,7 @@ def make_inputs(cfg: MoEConfig, with_experts: bool = True, threads: int | None =
         "w_router": make_w_router(cfg),
         "sel_bias": make_sel_bias(cfg),
         "logit_offset": make_logit_offset(cfg),
+        "norm_gain": make_norm_gain(cfg),
     }
     if with_experts:
         for t in EXPERT_TENSORS:

@@ -25,6 +25,13 @@ What the layer computes (all citations are to the pages' component tables):
   of intermediate size 2,048 (Qwen3.8 2.4T A95B atlas page, raw config
   shared_expert_intermediate_size).  Reading: its output is added with weight 1, outside
   the renormalized routed mixture, and it has no router row.
+* Pre-norm (optional, the step before the layer).  Each block's branch input is the
+  RMS-normalized residual stream ("Qwen3.5-397B-A17B vs Inkling" and "Qwen3.8-2.4T-A95B vs
+  Inkling", residual-stream rows: pre-norm blocks; RMSNorm in the block diagrams).
+  Qwen3.8's gains are zero-centred (same row), i.e. the scale is 1 + g, and its epsilon is
+  1e-6 (Qwen3.8 2.4T A95B atlas page, raw config rms_norm_eps).  RMSNorm itself is the
+  standard y = x / sqrt(mean(x^2) + eps) * gain.  bf16 layers take the normalized x
+  rounded once to bf16 (nearest even) as their input.
 * Experts.  SwiGLU FFNs: E(x) = W_down (SiLU(W_gate x) * W_up x), SiLU(z) = z / (1 + e^-z)
   (Inkling vs Gemma 4 31B, routed-expert and shared-expert rows; Qwen3.8 2.4T A95B atlas
   page, key facts "Activation silu" and raw config hidden_act).
@@ -58,8 +65,11 @@ import numpy as np
 
 # ----------------------------------------------------------------------------- numbers
 def promote(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float64 value of stored inputs: bf16 bit patterns (uint16) or float32."""
+    """Exact float64 value of stored inputs: bf16 bit patterns (uint16) or float32.
+    float64 arrays (values the oracle computed itself) pass through unchanged."""
     a = np.asarray(a)
+    if a.dtype == np.float64:
+        return a
     if dtype == "bf16":
         assert a.dtype == np.uint16, a.dtype
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
@@ -91,6 +101,26 @@ def softmax(z: np.ndarray) -> np.ndarray:
     z = z - z.max(axis=-1, keepdims=True)
     ez = np.exp(z)
     return ez / ez.sum(axis=-1, keepdims=True)
+
+
+# ----------------------------------------------------------------------------- pre-norm
+def rmsnorm(x64: np.ndarray, gain64: np.ndarray, eps: float, gain_offset: float) -> np.ndarray:
+    """RMSNorm of each row: x / sqrt(mean over the row of x^2 + eps) * (gain_offset + g).
+    gain_offset is 1 for zero-centred gains (Qwen3.8), 0 for plain gains."""
+    ms = np.mean(x64 * x64, axis=1, keepdims=True)
+    return x64 / np.sqrt(ms + eps) * (gain_offset + gain64)
+
+
+def prenorm_input(cfg, x, gain, eps: float, gain_offset: float, mode: str = "bf16_flow",
+                  tokens=None) -> np.ndarray:
+    """The layer's input for pre-norm blocks: RMSNorm of the raw hidden states x (all
+    tokens, or the listed ones), as float64 values; bf16 layers in bf16-flow mode round
+    it once to bf16, the precision in which the experts and the router read it."""
+    xs = x if tokens is None else x[np.asarray(tokens)]
+    y = rmsnorm(promote(xs, cfg.dtype), promote(gain, cfg.dtype), eps, gain_offset)
+    if mode == "bf16_flow" and cfg.dtype == "bf16":
+        y = round_to_bf16(y)
+    return y
 
 
 # ----------------------------------------------------------------------------- router
@@ -205,6 +235,17 @@ class OracleOut:
     y: np.ndarray        # [n_tokens, d] branch output (plus residual if given)
     tokens: np.ndarray   # the token indices the rows of y belong to
     routing: Routing     # routing of those tokens
+
+
+def moe_forward_prenorm(cfg, inputs: dict, gain, eps: float, gain_offset: float,
+                        mode: str = "bf16_flow", tokens=None, residual=None) -> OracleOut:
+    """The pre-norm block's branch: the layer applied to RMSNorm(x) (``prenorm_input``);
+    ``inputs["x"]`` holds the raw hidden states.  The residual, if given, is added to the
+    layer's output as in ``moe_forward``."""
+    tok = np.arange(inputs["x"].shape[0]) if tokens is None else np.asarray(tokens)
+    xn = np.zeros((inputs["x"].shape[0], cfg.d))
+    xn[tok] = prenorm_input(cfg, inputs["x"], gain, eps, gain_offset, mode, tokens=tok)
+    return moe_forward(cfg, dict(inputs, x=xn), mode=mode, tokens=tok, residual=residual)
 
 
 def moe_forward(cfg, inputs: dict, mode: str = "bf16_flow", tokens=None,

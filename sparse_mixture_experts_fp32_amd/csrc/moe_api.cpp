@@ -13,6 +13,7 @@ namespace {
 using moe::PlanEntry;
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxNormWidth = 16384;   // rmsnorm_kernel: 256 threads x 8 runs of 8
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -21,7 +22,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct Layout {
   int nsplit = 1, kchunk = 0;
   size_t part = 0, idx = 0, wts = 0, counts = 0, offsets = 0, row_token = 0, slot_row = 0,
-         hist = 0, plan = 0, h = 0, y = 0, total = 0;
+         hist = 0, plan = 0, h = 0, y = 0, xn = 0, total = 0;
 };
 
 struct Dims {
@@ -82,6 +83,7 @@ Layout layout_of(const moe_config_t& c, int64_t T) {
   L.plan = take(sizeof(PlanEntry) * moe::plan_entries(m.R, m.G));
   L.h = take(esize * m.R * moe::h_pitch(m.I));
   L.y = take(sizeof(float) * m.R * m.d);
+  L.xn = take(esize * m.T * m.d);   // normalized input of moe_forward_rmsnorm
   L.total = off;
   return L;
 }
@@ -311,6 +313,49 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x,
   MOE_TRY(do_permute(*cfg, T, idx, counts, offsets, row_token, slot_row, ws, stream));
   MOE_TRY(do_grouped(*cfg, T, x, offsets, row_token, w_gate, w_up, w_down, y, ws, stream));
   return do_combine(*cfg, T, y, slot_row, wts, residual, out, stream);
+}
+
+moe_status_t moe_rmsnorm(const moe_config_t* cfg, int64_t T, const void* x,
+                         const void* gain, float eps, int32_t zero_centred, void* y,
+                         hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_tokens(*cfg, T));
+  if (!std::isfinite(eps) || !(eps > 0.0f) || (zero_centred != 0 && zero_centred != 1))
+    return MOE_ERR_ARG;
+  if (cfg->d_model > kMaxNormWidth) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || gain == nullptr || y == nullptr) return MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(gain) || !aligned16(y)) return MOE_ERR_ARG;
+  (void)hipGetLastError();
+  return finish(moe::launch_rmsnorm(cfg->dtype, x, gain, y, (int)T, cfg->d_model, eps,
+                                    zero_centred ? 1.0f : 0.0f, stream),
+                stream);
+}
+
+moe_status_t moe_forward_rmsnorm(const moe_config_t* cfg, int64_t T, const void* x,
+                                 const void* norm_gain, float eps, int32_t zero_centred,
+                                 const void* w_router, const float* sel_bias,
+                                 const float* logit_offset, const void* w_gate,
+                                 const void* w_up, const void* w_down, const float* residual,
+                                 float* out, int32_t* topk_idx_out, int32_t* counts_out,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_tokens(*cfg, T));
+  if (!std::isfinite(eps) || !(eps > 0.0f) || (zero_centred != 0 && zero_centred != 1))
+    return MOE_ERR_ARG;
+  if (cfg->d_model > kMaxNormWidth) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || norm_gain == nullptr || !aligned16(x) || !aligned16(norm_gain))
+    return MOE_ERR_ARG;
+  MOE_TRY(check_ws(*cfg, T, ws, ws_bytes));
+  (void)hipGetLastError();
+  const Layout L = layout_of(*cfg, T);
+  void* xn = at<void>(ws, L.xn);
+  MOE_TRY(finish(moe::launch_rmsnorm(cfg->dtype, x, norm_gain, xn, (int)T, cfg->d_model, eps,
+                                     zero_centred ? 1.0f : 0.0f, stream),
+                 stream));
+  return moe_forward(cfg, T, xn, w_router, sel_bias, logit_offset, w_gate, w_up, w_down,
+                     residual, out, topk_idx_out, counts_out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

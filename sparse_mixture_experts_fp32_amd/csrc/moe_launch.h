@@ -19,6 +19,10 @@ struct PlanEntry {   // one m-tile of the grouped GEMM
   int32_t group, row0, nrows, pad;
 };
 
+// Pre-norm RMSNorm: y = x / sqrt(mean(x^2) + eps) * (gain_offset + gain), per token.
+hipError_t launch_rmsnorm(int dtype, const void* x, const void* gain, void* y, int T, int d,
+                          float eps, float gain_offset, hipStream_t stream);
+
 // Router partial logits: part[s][t][e] = sum over the s-th K chunk of x[t] . w_router[e].
 hipError_t launch_router_logits(int dtype, const void* x, const void* w_router, float* part,
                                 int T, int d, int NE, int nsplit, int kchunk,

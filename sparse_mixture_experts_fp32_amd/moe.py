@@ -76,6 +76,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_grouped_swiglu": [CFG, I64, P, P, P, P, P, P, P, P, SZ, P],
         "moe_combine": [CFG, I64, P, P, P, P, P, P],
         "moe_forward": [CFG, I64, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_rmsnorm": [CFG, I64, P, P, ctypes.c_float, ctypes.c_int32, P, P],
+        "moe_forward_rmsnorm": [CFG, I64, P, P, ctypes.c_float, ctypes.c_int32, P, P, P, P,
+                                P, P, P, P, P, P, P, SZ, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -159,3 +162,18 @@ def moe_forward(cfg, T, x, w_router, sel_bias, logit_offset, w_gate, w_up, w_dow
                                       _ptr(w_up), _ptr(w_down), _ptr(residual), _ptr(out),
                                       _ptr(topk_idx_out), _ptr(counts_out), _ptr(ws),
                                       ws_bytes, _stream(stream)))
+
+
+def moe_rmsnorm(cfg, T, x, gain, eps, zero_centred, y, stream=None):
+    _check(load_library().moe_rmsnorm(ctypes.byref(cfg), T, _ptr(x), _ptr(gain), float(eps),
+                                      int(zero_centred), _ptr(y), _stream(stream)))
+
+
+def moe_forward_rmsnorm(cfg, T, x, norm_gain, eps, zero_centred, w_router, sel_bias,
+                        logit_offset, w_gate, w_up, w_down, residual, out, topk_idx_out,
+                        counts_out, ws, ws_bytes, stream=None):
+    _check(load_library().moe_forward_rmsnorm(
+        ctypes.byref(cfg), T, _ptr(x), _ptr(norm_gain), float(eps), int(zero_centred),
+        _ptr(w_router), _ptr(sel_bias), _ptr(logit_offset), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(residual), _ptr(out), _ptr(topk_idx_out), _ptr(counts_out),
+        _ptr(ws), ws_bytes, _stream(stream)))

@@ -50,7 +50,8 @@ def workspace(cfg, T, torch):
 
 
 def run_forward(c, dev: dict, torch, residual=None, ws=None):
-    """moe_forward on device tensors; returns (out, topk_idx, counts) device tensors."""
+    """moe_forward (moe_forward_rmsnorm for pre-norm workloads, whose x is the raw hidden
+    state) on device tensors; returns (out, topk_idx, counts) device tensors."""
     cfg = cfg_struct(c)
     T = dev["x"].shape[0]
     if ws is None:
@@ -59,9 +60,15 @@ def run_forward(c, dev: dict, torch, residual=None, ws=None):
     out = torch.empty((T, c.d), dtype=torch.float32, device="cuda")
     idx = torch.empty((T, c.k), dtype=torch.int32, device="cuda")
     counts = torch.empty((c.E + c.S,), dtype=torch.int32, device="cuda")
-    M.moe_forward(cfg, T, dev["x"], dev["w_router"], dev.get("sel_bias"),
-                  dev.get("logit_offset"), dev["w_gate"], dev["w_up"], dev["w_down"],
-                  residual, out, idx, counts, buf, n)
+    if c.prenorm:
+        M.moe_forward_rmsnorm(cfg, T, dev["x"], dev["norm_gain"], c.norm_eps,
+                              c.norm_zero_centred, dev["w_router"], dev.get("sel_bias"),
+                              dev.get("logit_offset"), dev["w_gate"], dev["w_up"],
+                              dev["w_down"], residual, out, idx, counts, buf, n)
+    else:
+        M.moe_forward(cfg, T, dev["x"], dev["w_router"], dev.get("sel_bias"),
+                      dev.get("logit_offset"), dev["w_gate"], dev["w_up"], dev["w_down"],
+                      residual, out, idx, counts, buf, n)
     return out, idx, counts
 
 
@@ -85,9 +92,10 @@ def host_grouping(idx: np.ndarray, E: int, S: int):
 
 
 class StagedRunner:
-    """The layer as the four staged entry points, in the launch configuration the bench
-    times: moe_route -> moe_permute -> moe_grouped_swiglu -> moe_combine on one stream,
-    with preallocated outputs and one workspace."""
+    """The layer as the staged entry points, in the launch configuration the bench times:
+    [moe_rmsnorm ->] moe_route -> moe_permute -> moe_grouped_swiglu -> moe_combine on one
+    stream, with preallocated outputs and one workspace.  Pre-norm workloads normalize
+    the raw hidden states into a separate buffer first."""
 
     def __init__(self, c, dev: dict, torch):
         self.c, self.dev, self.torch = c, dev, torch
@@ -107,12 +115,18 @@ class StagedRunner:
         self.slot_row = torch.empty((R,), dtype=torch.int32, **e)
         self.y_rows = torch.empty((R, c.d), dtype=torch.float32, **e)
         self.out = torch.empty((T, c.d), dtype=torch.float32, **e)
+        self.xn = torch.empty_like(dev["x"]) if c.prenorm else None
 
     def step(self, stream, ev=None, residual=None):
         d, c, T, cfg = self.dev, self.c, self.T, self.cfg
         if ev is not None:
             ev[0].record(stream)
-        M.moe_route(cfg, T, d["x"], d["w_router"], d.get("sel_bias"), d.get("logit_offset"),
+        x = d["x"]
+        if c.prenorm:
+            M.moe_rmsnorm(cfg, T, x, d["norm_gain"], c.norm_eps, c.norm_zero_centred,
+                          self.xn, stream)
+            x = self.xn
+        M.moe_route(cfg, T, x, d["w_router"], d.get("sel_bias"), d.get("logit_offset"),
                     self.idx, self.w, self.ws, self.nws, stream)
         if ev is not None:
             ev[1].record(stream)
@@ -120,7 +134,7 @@ class StagedRunner:
                       self.slot_row, self.ws, self.nws, stream)
         if ev is not None:
             ev[2].record(stream)
-        M.moe_grouped_swiglu(cfg, T, d["x"], self.offsets, self.row_token, d["w_gate"],
+        M.moe_grouped_swiglu(cfg, T, x, self.offsets, self.row_token, d["w_gate"],
                              d["w_up"], d["w_down"], self.y_rows, self.ws, self.nws, stream)
         if ev is not None:
             ev[3].record(stream)

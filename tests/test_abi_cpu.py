@@ -28,7 +28,8 @@ def test_library_exports_every_declared_function():
     lib = M.load_library()
     names = M.header_functions()
     assert set(names) == {"moe_status_str", "moe_workspace_size", "moe_route", "moe_permute",
-                          "moe_grouped_swiglu", "moe_combine", "moe_forward"}
+                          "moe_grouped_swiglu", "moe_combine", "moe_forward", "moe_rmsnorm",
+                          "moe_forward_rmsnorm"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -120,6 +121,31 @@ def test_entry_points_validate_before_launch():
     qcfg = cfg_of(q)
     qneed = M.moe_workspace_size(qcfg, 8)
     assert status(M.moe_route, qcfg, 8, A, A, A, None, A, A, A, qneed) == M.MOE_ERR_ARG
+
+
+def test_rmsnorm_entry_points_validate_before_launch():
+    c = CONFIGS["inkling_decode"]
+    cfg = cfg_of(c)
+    need = M.moe_workspace_size(cfg, c.T)
+
+    def status(fn, *args):
+        with pytest.raises(M.MoEError) as ei:
+            fn(*args, stream=0)
+        return ei.value.status
+
+    assert status(M.moe_rmsnorm, cfg, 4, A, A, 0.0, 0, A) == M.MOE_ERR_ARG        # eps
+    assert status(M.moe_rmsnorm, cfg, 4, A, A, float("nan"), 0, A) == M.MOE_ERR_ARG
+    assert status(M.moe_rmsnorm, cfg, 4, A, A, 1e-6, 2, A) == M.MOE_ERR_ARG        # flag
+    assert status(M.moe_rmsnorm, cfg, 4, None, A, 1e-6, 0, A) == M.MOE_ERR_ARG
+    assert status(M.moe_rmsnorm, cfg, 4, A + 8, A, 1e-6, 0, A) == M.MOE_ERR_ARG
+    wide = cfg_of(c, d_model=16640)
+    assert status(M.moe_rmsnorm, wide, 4, A, A, 1e-6, 0, A) == M.MOE_ERR_UNSUPPORTED
+    assert status(M.moe_forward_rmsnorm, cfg, c.T, A, A, 1e-6, 1, A, None, None, A, A, A,
+                  None, A, None, None, A, need - 1) == M.MOE_ERR_WORKSPACE
+    assert status(M.moe_forward_rmsnorm, cfg, c.T, A, None, 1e-6, 1, A, None, None, A, A,
+                  A, None, A, None, None, A, need) == M.MOE_ERR_ARG
+    # T = 0 is a no-op
+    M.moe_rmsnorm(cfg, 0, None, None, 1e-6, 0, None, stream=0)
 
 
 def test_zero_tokens_is_a_no_op():

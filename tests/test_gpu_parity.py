@@ -16,7 +16,7 @@ from gpu_util import (StagedRunner, cfg_struct, device_inputs, host_grouping,  #
                       run_forward, to_dev, workspace)
 from moe_inputs import CONFIGS, MoEConfig, make_inputs  # noqa: E402
 from oracle import moe_oracle as O  # noqa: E402
-from parity import assert_outputs, check_routing, output_metrics  # noqa: E402
+from parity import GAP, assert_outputs, check_routing, output_metrics  # noqa: E402
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -65,6 +65,26 @@ SMALL = {c.name: c for c in [
           seed=23).with_(S=1),
 ]}
 
+# Pre-norm shapes: x is the raw hidden state; the layer runs on RMSNorm(x).
+PRENORM = {c.name: c for c in [
+    small("pre_sig_bf16", "sigmoid", "bf16", T=300, d=512, E=40, S=2, I=256, k=6,
+          seed=24).with_(prenorm=True),
+    small("pre_soft_bf16_zc", "softmax", "bf16", T=257, d=768, E=64, S=0, I=384, k=8,
+          seed=25).with_(S=1, prenorm=True, norm_zero_centred=True),
+    small("pre_sig_f32_zc", "sigmoid", "f32", T=100, d=256, E=20, S=3, I=128, k=4,
+          seed=26).with_(prenorm=True, norm_zero_centred=True),
+    # The Kimi K3 routing shape (sigmoid 16 of 896) at a small width and T.
+    small("pre_kimi_routing", "sigmoid", "bf16", T=512, d=1024, E=896, S=0, I=128, k=16,
+          seed=27).with_(prenorm=True),
+]}
+# Widest supported RMSNorm row (RMSNorm stage only).
+NORM_WIDE = small("norm_wide", "sigmoid", "bf16", T=64, d=16384, E=8, S=0, I=128, k=2,
+                  seed=28).with_(prenorm=True, norm_zero_centred=True)
+# A one-ulp difference of a bf16 normalized input (f32 statistic on the GPU, float64 in
+# the oracle) moves a logit by up to ~1e-4; near-ties below this are excluded on pre-norm
+# paths (and must still be valid alternatives).
+PRENORM_GAP = 1e-4
+
 _cache = {}
 
 
@@ -92,6 +112,52 @@ def test_forward_small(name):
     assert (counts[:c.E] == np.bincount(idx.ravel(), minlength=c.E)).all()
     assert (counts[c.E:] == c.T).all()
     mx, mn = assert_outputs(out[~excl], ref.y[~excl], f"{name} forward")
+    log(f"{name}: excluded {excl.sum()}/{c.T}, max rel {mx:.2e}, mean rel {mn:.2e}")
+
+
+def bf16_bits_to_f64(t):
+    u = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32)
+    return (u << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("name", list(PRENORM) + ["norm_wide"])
+def test_rmsnorm_stage(name):
+    c = PRENORM.get(name, NORM_WIDE)
+    inp = make_inputs(c, with_experts=False)
+    x, gain = to_dev(inp["x"], torch), to_dev(inp["norm_gain"], torch)
+    y = torch.empty_like(x)
+    M.moe_rmsnorm(cfg_struct(c), c.T, x, gain, c.norm_eps, c.norm_zero_centred, y)
+    torch.cuda.synchronize()
+    off = 1.0 if c.norm_zero_centred else 0.0
+    ref = O.prenorm_input(c, inp["x"], inp["norm_gain"], c.norm_eps, off, mode=mode_of(c))
+    if c.dtype == "bf16":
+        g = bf16_bits_to_f64(y)
+        # at most one bf16 step apart, and rarely that
+        ulp = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 8)
+        diff = np.abs(g - ref)
+        assert (diff <= ulp).all(), diff.max()
+        assert (diff > 0).mean() < 1e-2, (diff > 0).mean()
+    else:
+        np.testing.assert_allclose(y.cpu().numpy(), ref, rtol=2e-6, atol=0)
+
+
+@pytest.mark.parametrize("name", list(PRENORM))
+def test_forward_rmsnorm(name):
+    """moe_forward_rmsnorm against the oracle's pre-norm branch; the staged sequence
+    (moe_rmsnorm, then the four stages) must match it bit for bit."""
+    c = PRENORM[name]
+    inp, dev = inputs_of(c)
+    out, idx, counts = run_forward(c, dev, torch)
+    run = StagedRunner(c, dev, torch)
+    run.step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(out, run.out) and torch.equal(idx, run.idx)
+    out, idx, counts = out.cpu().numpy(), idx.cpu().numpy(), counts.cpu().numpy()
+    off = 1.0 if c.norm_zero_centred else 0.0
+    ref = O.moe_forward_prenorm(c, inp, inp["norm_gain"], c.norm_eps, off, mode=mode_of(c))
+    excl = check_routing(idx, ref.routing, c.E, gap=PRENORM_GAP)
+    assert (counts[:c.E] == np.bincount(idx.ravel(), minlength=c.E)).all()
+    mx, mn = assert_outputs(out[~excl], ref.y[~excl], f"{name} forward_rmsnorm")
     log(f"{name}: excluded {excl.sum()}/{c.T}, max rel {mx:.2e}, mean rel {mn:.2e}")
 
 
@@ -220,7 +286,7 @@ def test_zero_router_tie_rule_on_gpu():
 
 # ------------------------------------------------------------------------ full size
 FULL_SAMPLE = {"inkling_decode": None, "inkling_prefill": 48, "qwen38": 24,
-               "inkling_skewed": 48, "qwen38_shared": 24}
+               "inkling_skewed": 48, "qwen38_shared": 24, "kimi_k3_latent": 48}
 
 
 @pytest.mark.parametrize("name", list(FULL_SAMPLE))
@@ -248,15 +314,20 @@ def test_full_size(name):
     del dev, run, fwd
     torch.cuda.empty_cache()
     log(f"[{name}] oracle routing")
-    r = O.route(c, inp["x"], inp["w_router"], inp["sel_bias"], inp["logit_offset"])
-    excl = check_routing(idx, r, c.E)
+    off = 1.0 if c.norm_zero_centred else 0.0
+    x_in = (O.prenorm_input(c, inp["x"], inp["norm_gain"], c.norm_eps, off) if c.prenorm
+            else inp["x"])
+    r = O.route(c, x_in, inp["w_router"], inp["sel_bias"], inp["logit_offset"])
+    excl = check_routing(idx, r, c.E, gap=PRENORM_GAP if c.prenorm else GAP)
     assert (counts[:c.E] == np.bincount(idx.ravel(), minlength=c.E)).all()
     ns = FULL_SAMPLE[name]
     cand = np.nonzero(~excl)[0]
     tokens = cand if ns is None else np.sort(
         np.random.default_rng(c.seed).choice(cand, size=ns, replace=False))
     log(f"[{name}] oracle outputs on {len(tokens)} tokens")
-    ref = O.moe_forward(c, inp, mode="bf16_flow", tokens=tokens)
+    ref = (O.moe_forward_prenorm(c, inp, inp["norm_gain"], c.norm_eps, off,
+                                 mode="bf16_flow", tokens=tokens) if c.prenorm
+           else O.moe_forward(c, inp, mode="bf16_flow", tokens=tokens))
     mx, mn = assert_outputs(out[tokens], ref.y, f"{name} forward")
     touched = int((counts[:c.E] > 0).sum())
     log(f"[{name}] excluded {excl.sum()}/{c.T}, touched {touched}, max count "

@@ -127,6 +127,43 @@ def test_round_to_bf16_matches_torch_on_float32():
     np.testing.assert_array_equal(mine, ref)
 
 
+# ---------------------------------------------------------------- pre-norm
+def test_rmsnorm_closed_form():
+    """x = (3, 4, 0, 0): mean of squares 25/4, rms 5/2, so x / rms = (1.2, 1.6, 0, 0);
+    zero-centred gains g scale by 1 + g, plain gains by g."""
+    x = np.array([[3.0, 4.0, 0.0, 0.0]])
+    g = np.array([0.5, -0.25, 2.0, 1.0])
+    np.testing.assert_allclose(O.rmsnorm(x, g, 0.0, 0.0), [[0.6, -0.4, 0, 0]], rtol=1e-15)
+    np.testing.assert_allclose(O.rmsnorm(x, g, 0.0, 1.0), [[1.8, 1.2, 0, 0]], rtol=1e-15)
+    # eps enters under the root: mean 25/4 + 3/4 = 7, rms sqrt(7)
+    np.testing.assert_allclose(O.rmsnorm(x, np.ones(4), 0.75, 0.0),
+                               [[3 / math.sqrt(7), 4 / math.sqrt(7), 0, 0]], rtol=1e-15)
+
+
+def test_rmsnorm_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((64, 384)) * 3.0
+    g = rng.standard_normal(384) * 0.1
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (384,), torch.from_numpy(1 + g),
+                                       eps=1e-6).numpy()
+    np.testing.assert_allclose(O.rmsnorm(x, g, 1e-6, 1.0), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_rmsnorm_scale_invariance_and_prenorm_rounding():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((16, 64))
+    g = 1 + 0.1 * rng.standard_normal(64)
+    np.testing.assert_allclose(O.rmsnorm(1e3 * x, g, 0.0, 0.0), O.rmsnorm(x, g, 0.0, 0.0),
+                               rtol=1e-13)
+    cfg = small_cfg("sigmoid", dtype="bf16", T=16, d=64).with_(prenorm=True)
+    inp = make_inputs(cfg, with_experts=False)
+    xn = O.prenorm_input(cfg, inp["x"], inp["norm_gain"], cfg.norm_eps, 0.0)
+    exact = O.prenorm_input(cfg, inp["x"], inp["norm_gain"], cfg.norm_eps, 0.0, mode="exact")
+    assert (O.round_to_bf16(exact) == xn).all()
+    assert 0 < np.abs(xn - exact).max() <= 2.0 ** -8 * np.abs(exact).max()
+
+
 # ---------------------------------------------------------------- router
 def test_topk_brute_force_subsets():
     rng = np.random.default_rng(1)
