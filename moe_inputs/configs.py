@@ -40,6 +40,7 @@ class MoEConfig:
     prenorm: bool = False         # x is the raw hidden state; the layer input is RMSNorm(x)
     norm_zero_centred: bool = False  # RMSNorm scale is 1 + g (stored g) instead of g
     norm_eps: float = 1e-6
+    weight_format: str = "dense"  # routed experts' weights: "dense" (dtype) or "mxfp4"
 
     @property
     def route_scale(self) -> float:
@@ -91,6 +92,9 @@ CONFIGS: dict[str, MoEConfig] = {
     # the 8 hottest experts.
     "inkling_skewed": MoEConfig(name="inkling_skewed", T=16384, seed=4,
                                 **{**_INKLING, "zipf_s": 1.2, "zipf_hot_share": 0.30}),
+    # Inkling decode batch with MXFP4 routed-expert weights (shared experts stay bf16).
+    "inkling_decode_mxfp4": MoEConfig(name="inkling_decode_mxfp4", T=32, seed=7,
+                                      weight_format="mxfp4", **_INKLING),
     # Kimi K3-style latent experts: sigmoid 16-of-896 in a 3,584-wide latent, RMSNorm
     # before the experts' up-projection (plain gains); I = 3,072 is a reading (the pages
     # give none; 2.8T parameters over 93 layers of 896 x 3 x 3,584 x I suggest ~3,100).
@@ -103,5 +107,5 @@ CONFIGS: dict[str, MoEConfig] = {
 # The order in which the five workloads are listed everywhere.
 CONFIG_ORDER = ["tiny_fp32", "inkling_decode", "inkling_prefill", "qwen38", "inkling_skewed"]
 # Workloads beyond the five above: Qwen3.8 with its ungated shared expert; Kimi K3-style
-# latent experts behind a pre-norm RMSNorm.
-EXTRA_ORDER = ["qwen38_shared", "kimi_k3_latent"]
+# latent experts behind a pre-norm RMSNorm; the Inkling decode batch with MXFP4 weights.
+EXTRA_ORDER = ["qwen38_shared", "kimi_k3_latent", "inkling_decode_mxfp4"]

@@ -20,6 +20,9 @@ Layouts (row-major, contiguous):
   w_gate     [E + S, I, d]
   w_up       [E + S, I, d]
   w_down     [E + S, d, I]
+MXFP4 workloads (routed experts only; ``w_*`` then hold the S shared experts):
+  wq_gate, wq_up [E, I, d/2] uint8 codes;  ws_gate, ws_up [E, I, d/32] uint8 scales
+  wq_down        [E, d, I/2] uint8 codes;  ws_down        [E, d, I/32] uint8 scales
 """
 from __future__ import annotations
 
@@ -169,8 +172,64 @@ def fill_expert_tensor(cfg: MoEConfig, tensor: str, out: np.ndarray | None = Non
     return out
 
 
+# ----------------------------------------------------------------------------- MXFP4
+# OCP Microscaling FP4 (the checkpoint format the pages name for Inkling's and K3's
+# routed experts): 32 consecutive elements along K share one E8M0 scale byte s (scale
+# 2^(s - 127)); each element is an E2M1 code (sign, 2 exponent bits, 1 mantissa bit), two
+# codes per byte, element 2i in the low nibble.  Quantizing is input preparation here
+# (the weights arrive quantized), not a step of the layer.
+_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float64)
+MX_BLOCK = 32
+
+
+def quantize_mxfp4(w: np.ndarray):
+    """float32 [..., K] -> (codes uint8 [..., K/2], scales uint8 [..., K/32]).  Per block,
+    s = floor(log2(amax)) - 2 + 127 (amax / scale in [4, 8)); elements round to the
+    nearest E2M1 magnitude, ties to the even code, saturating at 6."""
+    w = np.asarray(w, np.float64)
+    K = w.shape[-1]
+    blocks = w.reshape(w.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(blocks).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    s = np.clip(e + 127, 0, 254).astype(np.int64)
+    a = np.abs(blocks) / np.ldexp(1.0, s - 127)[..., None]
+    lo = np.clip(np.searchsorted(_E2M1_MAG, a, side="right") - 1, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    d_lo, d_hi = a - _E2M1_MAG[lo], _E2M1_MAG[hi] - a
+    up = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    mag = np.where(a >= 6.0, 7, np.where(up, hi, lo))
+    code = (mag | np.where(blocks < 0, 8, 0)).astype(np.uint8)
+    code = code.reshape(w.shape)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return packed, s.astype(np.uint8)
+
+
+def make_expert_mxfp4(cfg: MoEConfig, tensor: str, e: int):
+    """Routed expert e's ``tensor`` in MXFP4: the same N(0, w_std^2) stream as the dense
+    workloads, in float32, quantized."""
+    return quantize_mxfp4(_draw(_rng(cfg.seed, tensor, e), expert_shape(cfg, tensor),
+                                cfg.w_std, "f32"))
+
+
+def fill_expert_mxfp4(cfg: MoEConfig, tensor: str, threads: int | None = None):
+    """(codes [E, N, K/2], scales [E, N, K/32]) of every routed expert."""
+    N, K = expert_shape(cfg, tensor)
+    codes = np.empty((cfg.E, N, K // 2), np.uint8)
+    scales = np.empty((cfg.E, N, K // MX_BLOCK), np.uint8)
+
+    def one(e):
+        codes[e], scales[e] = make_expert_mxfp4(cfg, tensor, e)
+
+    with ThreadPoolExecutor(threads or default_threads()) as ex:
+        list(ex.map(one, range(cfg.E)))
+    return codes, scales
+
+
 def make_inputs(cfg: MoEConfig, with_experts: bool = True, threads: int | None = None) -> dict:
-    """All inputs of one workload as host arrays (bf16 as uint16 bits)."""
+    """All inputs of one workload as host arrays (bf16 as uint16 bits).  MXFP4 workloads
+    hold the routed experts as ``wq_<tensor>`` (codes) and ``ws_<tensor>`` (scales) and
+    only the S shared experts in ``w_<tensor>``."""
     inp = {
         "x": make_x(cfg),
         "w_router": make_w_router(cfg),
@@ -178,7 +237,14 @@ def make_inputs(cfg: MoEConfig, with_experts: bool = True, threads: int | None =
         "logit_offset": make_logit_offset(cfg),
         "norm_gain": make_norm_gain(cfg),
     }
-    if with_experts:
+    if with_experts and cfg.weight_format == "mxfp4":
+        for t in EXPERT_TENSORS:
+            inp["wq_" + t[2:]], inp["ws_" + t[2:]] = fill_expert_mxfp4(cfg, t, threads)
+            shared = np.empty((cfg.S,) + expert_shape(cfg, t), storage_dtype(cfg))
+            for s_ in range(cfg.S):
+                shared[s_] = make_expert(cfg, t, cfg.E + s_)
+            inp[t] = shared
+    elif with_experts:
         for t in EXPERT_TENSORS:
             inp[t] = fill_expert_tensor(cfg, t, threads=threads)
     return inp

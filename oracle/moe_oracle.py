@@ -32,6 +32,13 @@ What the layer computes (all citations are to the pages' component tables):
   1e-6 (Qwen3.8 2.4T A95B atlas page, raw config rms_norm_eps).  RMSNorm itself is the
   standard y = x / sqrt(mean(x^2) + eps) * gain.  bf16 layers take the normalized x
   rounded once to bf16 (nearest even) as their input.
+* MXFP4 expert weights (optional).  The pages name block-scaled FP4 (MXFP4/NVFP4) for
+  Inkling's routed experts (Qwen3.5-397B-A17B vs Inkling, block diagram, low-precision
+  training box; Inkling vs Gemma 4 31B, shared-expert row: the shared experts stay BF16 in
+  the FP4 checkpoint) but do not define the format; the OCP Microscaling definition is
+  used: blocks of 32 elements along K, an E8M0 scale 2^(s - 127) per block, E2M1 elements
+  (sign, 2 exponent bits with bias 1, 1 mantissa bit).  The layer then runs on the exact
+  dequantized weights.
 * Experts.  SwiGLU FFNs: E(x) = W_down (SiLU(W_gate x) * W_up x), SiLU(z) = z / (1 + e^-z)
   (Inkling vs Gemma 4 31B, routed-expert and shared-expert rows; Qwen3.8 2.4T A95B atlas
   page, key facts "Activation silu" and raw config hidden_act).
@@ -121,6 +128,49 @@ def prenorm_input(cfg, x, gain, eps: float, gain_offset: float, mode: str = "bf1
     if mode == "bf16_flow" and cfg.dtype == "bf16":
         y = round_to_bf16(y)
     return y
+
+
+# ----------------------------------------------------------------------------- MXFP4
+def e2m1_value(code: np.ndarray) -> np.ndarray:
+    """E2M1 element value from its 4-bit code: sign bit 3, exponent bits 2..1 (bias 1),
+    mantissa bit 0; exponent 0 is subnormal (0 or 0.5)."""
+    code = np.asarray(code, np.int64)
+    sign = np.where(code & 8, -1.0, 1.0)
+    e = (code >> 1) & 3
+    m = code & 1
+    mag = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.ldexp(1.0, e - 1))
+    return sign * mag
+
+
+def e8m0_value(s: np.ndarray) -> np.ndarray:
+    """E8M0 scale: 2^(s - 127); s = 255 is NaN."""
+    s = np.asarray(s, np.int64)
+    return np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
+
+
+def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """[..., K/2] packed codes (element 2i in the low nibble) and [..., K/32] scales ->
+    float64 [..., K]."""
+    codes = np.asarray(codes, np.uint8)
+    el = np.empty(codes.shape[:-1] + (2 * codes.shape[-1],), np.int64)
+    el[..., 0::2] = codes & 0xF
+    el[..., 1::2] = codes >> 4
+    v = e2m1_value(el)
+    K = v.shape[-1]
+    v = v.reshape(v.shape[:-1] + (K // 32, 32)) * e8m0_value(scales)[..., None]
+    return v.reshape(v.shape[:-2] + (K,))
+
+
+def expert_weights(cfg, inputs: dict, e: int):
+    """(W_gate, W_up, W_down) of expert e as float64: MXFP4 workloads keep the routed
+    experts quantized (``wq_*`` codes, ``ws_*`` scales) and the shared experts, like every
+    dense workload, in ``w_*`` (shared expert s at index s there)."""
+    if getattr(cfg, "weight_format", "dense") == "mxfp4":
+        if e < cfg.E:
+            return tuple(dequant_mxfp4(inputs["wq_" + t][e], inputs["ws_" + t][e])
+                         for t in ("gate", "up", "down"))
+        e = e - cfg.E
+    return tuple(promote(inputs["w_" + t][e], cfg.dtype) for t in ("gate", "up", "down"))
 
 
 # ----------------------------------------------------------------------------- router
@@ -258,7 +308,7 @@ def moe_forward(cfg, inputs: dict, mode: str = "bf16_flow", tokens=None,
     ``forced_idx`` [n, k] replaces the oracle's own routed selection (weights are then
     those of the forced set).
     ``inputs`` holds the generator's arrays: x, w_router, sel_bias, logit_offset,
-    w_gate, w_up, w_down."""
+    w_gate, w_up, w_down (and wq_* / ws_* for MXFP4 routed experts)."""
     x = inputs["x"]
     tok = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
     r = route(cfg, x, inputs["w_router"], inputs.get("sel_bias"),
@@ -272,9 +322,8 @@ def moe_forward(cfg, inputs: dict, mode: str = "bf16_flow", tokens=None,
                                                     (n, cfg.S))], axis=1)
     for e in np.unique(active):
         rows, slots = np.nonzero(active == e)
-        out = swiglu_expert(x64[rows], promote(inputs["w_gate"][e], cfg.dtype),
-                            promote(inputs["w_up"][e], cfg.dtype),
-                            promote(inputs["w_down"][e], cfg.dtype), round_h)
+        wg, wu, wd = expert_weights(cfg, inputs, int(e))
+        out = swiglu_expert(x64[rows], wg, wu, wd, round_h)
         y[rows] += r.weights[rows, slots][:, None] * out
     if residual is not None:
         y = np.asarray(residual, dtype=np.float64)[tok] + y

@@ -164,6 +164,75 @@ def test_rmsnorm_scale_invariance_and_prenorm_rounding():
     assert 0 < np.abs(xn - exact).max() <= 2.0 ** -8 * np.abs(exact).max()
 
 
+# ---------------------------------------------------------------- MXFP4 weights
+def test_e2m1_code_table():
+    """The 16 E2M1 codes: sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0 is
+    subnormal.  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (the OCP MX element table)."""
+    want = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    got = O.e2m1_value(np.arange(16))
+    assert got[:8].tolist() == want
+    assert got[8:].tolist() == [-v for v in want]
+    assert math.copysign(1.0, got[8]) == -1.0          # code 8 is -0
+
+
+def test_e8m0_scale():
+    v = O.e8m0_value(np.array([0, 1, 126, 127, 128, 254, 255]))
+    assert v[:6].tolist() == [2.0 ** -127, 2.0 ** -126, 0.5, 1.0, 2.0, 2.0 ** 127]
+    assert np.isnan(v[6])
+
+
+def test_dequant_mxfp4_hand_example():
+    """Byte 0x21 holds element 0 = code 1 (0.5) in its low nibble and element 1 = code 2
+    (1.0) in its high nibble; byte 0xF8 holds -0 and -6.  Scale byte 128 doubles them."""
+    codes = np.zeros((1, 16), np.uint8)
+    codes[0, :2] = [0x21, 0xF8]
+    codes[0, 2] = 0x7F                                   # -6, then +6
+    v = O.dequant_mxfp4(codes, np.array([[128]], np.uint8))
+    assert v[0, :6].tolist() == [1.0, 2.0, -0.0, -12.0, -12.0, 12.0]
+    assert (v[0, 6:] == 0).all()
+    # A second block has its own scale.
+    codes2 = np.zeros((1, 32), np.uint8)
+    codes2[0, 16] = 0x33                                 # elements 32, 33 = 1.5 each
+    v2 = O.dequant_mxfp4(codes2, np.array([[127, 125]], np.uint8))
+    assert v2[0, 32:34].tolist() == [0.375, 0.375] and v2[0, :32].sum() == 0
+
+
+def test_mxfp4_round_trip_and_error_bound():
+    """The generator's quantizer (written separately) against the oracle's decoder:
+    grid values times a block scale come back exactly, and random weights land within
+    the format's step (at most 2 scale units, past the largest element 6)."""
+    from moe_inputs import quantize_mxfp4
+    rng = np.random.default_rng(9)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    exact = (rng.choice(grid, (8, 64)) * rng.choice([-1, 1], (8, 64))).astype(np.float32)
+    exact[:, 0] = 6.0                                    # pins each block's scale to 1
+    exact[:, 32] = -6.0
+    c, sc = quantize_mxfp4(exact)
+    assert (sc == 127).all()
+    np.testing.assert_array_equal(O.dequant_mxfp4(c, sc), exact)
+    w = (rng.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    c, sc = quantize_mxfp4(w)
+    err = np.abs(O.dequant_mxfp4(c, sc) - w).reshape(16, 8, 32)
+    scale = O.e8m0_value(sc)[..., None]
+    assert (err <= 2 * scale).all() and (err <= 0.5 * scale).mean() > 0.5
+
+
+def test_mxfp4_workload_uses_dequantized_routed_and_bf16_shared_weights():
+    cfg = small_cfg("sigmoid", dtype="bf16", T=12, d=64, E=6, S=1, I=32, k=2,
+                    seed=15).with_(weight_format="mxfp4")
+    inp = make_inputs(cfg)
+    assert inp["wq_gate"].shape == (6, 32, 32) and inp["ws_down"].shape == (6, 64, 1)
+    assert inp["w_gate"].shape == (1, 32, 64)
+    out = O.moe_forward(cfg, inp, mode="exact")
+    # The same layer with the dequantized weights stored densely (float64 passthrough).
+    dense = dict(inp)
+    for t in ("gate", "up", "down"):
+        deq = O.dequant_mxfp4(inp["wq_" + t], inp["ws_" + t])
+        dense["w_" + t] = np.concatenate([deq, O.promote(inp["w_" + t], "bf16")])
+    ref = O.moe_forward(cfg.with_(weight_format="dense"), dense, mode="exact")
+    np.testing.assert_allclose(out.y, ref.y, rtol=1e-13, atol=1e-15)
+
+
 # ---------------------------------------------------------------- router
 def test_topk_brute_force_subsets():
     rng = np.random.default_rng(1)
