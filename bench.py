@@ -127,7 +127,10 @@ def run(c, steps, warmup, torch):
     touched = int((cnt[:c.E] > 0).sum())
     esize = 2 if c.dtype == "bf16" else 4
     f_router, f_experts = layer_flops(c)
-    w_bytes = (touched + c.S) * 3 * c.d * c.I * esize
+    if c.weight_format == "mxfp4":   # routed: 4-bit codes + one scale byte per 32
+        w_bytes = touched * 3 * c.d * c.I * (0.5 + 1 / 32) + c.S * 3 * c.d * c.I * esize
+    else:
+        w_bytes = (touched + c.S) * 3 * c.d * c.I * esize
     alg_bytes = (w_bytes + (c.E + c.S) * c.d * esize + T * c.d * esize + T * c.d * 4)
     grouped_bytes = w_bytes + T * c.d * esize + R * c.d * 4
     ms = wall * 1e3 / steps

@@ -176,6 +176,40 @@ moe_status_t moe_forward_rmsnorm(const moe_config_t* cfg, int64_t T, const void*
                                  float* out, int32_t* topk_idx_out, int32_t* counts_out,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* MXFP4 routed experts (next to the decode shape's HBM bound: ~4.25 bits per weight).
+ * The routed experts' weights arrive block-scaled FP4: Inkling's FP4 checkpoint keeps its
+ * shared experts in BF16 ("Inkling vs Gemma 4 31B", shared-expert row) and the pages name
+ * MXFP4/NVFP4 ("Qwen3.5-397B-A17B vs Inkling", block diagram, FP4 training box) without
+ * defining it; the OCP Microscaling definition is used: per 32 consecutive K elements one
+ * E8M0 scale byte s (2^(s - 127), 255 = NaN), elements E2M1 (sign, 2 exponent bits with
+ * bias 1, 1 mantissa bit), two per byte with element 2i in the low nibble.  The experts
+ * compute on the exactly dequantized weights with bf16 x, as in moe_grouped_swiglu.
+ *   wq_gate, wq_up [E, I, d/2] uint8, ws_gate, ws_up [E, I, d/32] uint8;
+ *   wq_down [E, d, I/2] uint8, ws_down [E, d, I/32] uint8 (codes 16-byte aligned);
+ *   w_gate_shared, w_up_shared [S, I, d] bf16, w_down_shared [S, d, I] bf16 (NULL iff
+ *   S = 0).  bf16 layers only (MOE_ERR_UNSUPPORTED otherwise); 128-row tiles. */
+moe_status_t moe_grouped_swiglu_mxfp4(const moe_config_t* cfg, int64_t T, const void* x,
+                                      const int32_t* offsets, const int32_t* row_token,
+                                      const uint8_t* wq_gate, const uint8_t* ws_gate,
+                                      const uint8_t* wq_up, const uint8_t* ws_up,
+                                      const uint8_t* wq_down, const uint8_t* ws_down,
+                                      const void* w_gate_shared, const void* w_up_shared,
+                                      const void* w_down_shared, float* y_rows, void* ws,
+                                      size_t ws_bytes, hipStream_t stream);
+
+/* The whole layer with MXFP4 routed experts (arguments as in moe_forward and
+ * moe_grouped_swiglu_mxfp4). */
+moe_status_t moe_forward_mxfp4(const moe_config_t* cfg, int64_t T, const void* x,
+                               const void* w_router, const float* sel_bias,
+                               const float* logit_offset, const uint8_t* wq_gate,
+                               const uint8_t* ws_gate, const uint8_t* wq_up,
+                               const uint8_t* ws_up, const uint8_t* wq_down,
+                               const uint8_t* ws_down, const void* w_gate_shared,
+                               const void* w_up_shared, const void* w_down_shared,
+                               const float* residual, float* out, int32_t* topk_idx_out,
+                               int32_t* counts_out, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -74,6 +74,31 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t
 // and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// MXFP4 (OCP Microscaling FP4) decode.  E8M0 scale byte s -> 2^(s - 127) (s = 0 is the
+// f32 subnormal 2^-127, s = 255 NaN).  E2M1 code c: sign bit 3, exponent bits 2..1 (bias
+// 1), mantissa bit 0; exponent 0 is subnormal (0 or 0.5).
+__device__ __forceinline__ float mx_scale(uint32_t s) {
+  s &= 0xffu;
+  return __uint_as_float(s == 0 ? 0x00400000u : (s == 255 ? 0x7fc00000u : s << 23));
+}
+__device__ __forceinline__ float e2m1_f32(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const uint32_t mag = e ? ((126u + e) << 23) | (m << 22) : (m ? 0x3f000000u : 0u);
+  return __uint_as_float(mag | ((c & 8u) << 28));
+}
+// 8 codes (one 32-bit word, element i in bits 4i..4i+3) -> 8 bf16 (one 16-byte chunk,
+// element i in halfword i).
+__device__ __forceinline__ u32x4 mxfp4_chunk(uint32_t w, float sc) {
+  u32x4 o;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t lo = f32_to_bf16_rne(e2m1_f32((w >> (8 * p)) & 15u) * sc);
+    const uint32_t hi = f32_to_bf16_rne(e2m1_f32((w >> (8 * p + 4)) & 15u) * sc);
+    o[p] = lo | (hi << 16);
+  }
+  return o;
+}
+
 template <typename TE>
 struct Mfma;
 
@@ -121,7 +146,7 @@ __device__ __forceinline__ void store_h(float* p, float v) { *p = v; }
 // phases of 32 consecutive tiles.  Tiles take equal time, so the tiles of a phase run in
 // lockstep and the data they share (weight slices, gathered rows) is fetched into the
 // XCD's L2 once.
-template <typename TE, int MODE>
+template <typename TE, int MODE, bool FP4>
 __global__ __launch_bounds__(512) void grouped_gemm_kernel(
     const TE* __restrict__ a_src,           // MODE 0: x [T, K]; MODE 1: h [R, K]
     const int32_t* __restrict__ row_token,  // MODE 0 only
@@ -132,7 +157,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
     void* __restrict__ c_out,               // MODE 0: h [R, N] (TE); MODE 1: y [R, N] f32
     uint32_t a_bytes,                       // bytes of a_src
     int K, int N, int T, int NT,
-    int lda, int ldc) {                     // row pitch (elements) of a_src and c_out
+    int lda, int ldc,                       // row pitch (elements) of a_src and c_out
+    // FP4: the E routed experts' B in MXFP4 (codes [E, N, K/2], scales [E, N, K/32];
+    // MODE 0: q0/s0 gate, q1/s1 up; MODE 1: q0/s0 down); b0/b1 then hold only the shared
+    // experts, expert g >= E at index g - E.
+    const uint8_t* __restrict__ q0, const uint8_t* __restrict__ q1,
+    const uint8_t* __restrict__ s0, const uint8_t* __restrict__ s1, int E) {
   constexpr int EPC = 16 / sizeof(TE);  // elements per 16-byte chunk
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage];
 
@@ -208,13 +238,15 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
     }
     // gate/up: B-rows 0..127 (waves 0..3) are gate rows n0.., B-rows 128..255 (waves
     // 4..7) the up rows n0..;  down: B-rows 0..255 are w_down rows n0..
+    const bool quant = FP4 && g < E;          // tile-uniform
+    const int gb = FP4 ? (quant ? 0 : g - E) : g;   // index into b0 / b1 (dense tiles)
     const TE* bsrc;
     int brow0;
     if (MODE == 0) {
-      bsrc = (wv < 4 ? b0 : b1) + ((size_t)g * N + n0) * K;
+      bsrc = (wv < 4 ? b0 : b1) + ((size_t)gb * N + n0) * K;
       brow0 = 32 * (wv & 3);
     } else {
-      bsrc = b0 + ((size_t)g * N + n0) * K;
+      bsrc = b0 + ((size_t)gb * N + n0) * K;
       brow0 = 32 * wv;
     }
     const __amdgpu_buffer_rsrc_t b_rsrc =
@@ -294,6 +326,79 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
     }                                                                                   \
   } while (0)
 
+    if (FP4 && quant) {
+      // MXFP4 B: thread t stages B-row t / 2, elements 32 (t % 2) .. +32 of the 64-wide K
+      // step = one MX block: 16 bytes of codes and its scale byte, dequantized to bf16
+      // (exact in the normal range: 2 significant bits times a power of two) on the
+      // way into LDS chunks 4 (t % 2) .. +3 of that row.
+      const int qrow = tid >> 1, qhalf = tid & 1;
+      const int qlocal = MODE == 0 ? (qrow & (kGateUpBN - 1)) : qrow;
+      const uint8_t* qsrc = MODE == 0 ? (wv < 4 ? q0 : q1) : q0;
+      const uint8_t* ssrc = MODE == 0 ? (wv < 4 ? s0 : s1) : s0;
+      const int qrows = MODE == 0 ? kGateUpBN : kDownBN;
+      const __amdgpu_buffer_rsrc_t q_rsrc = buffer_rsrc(
+          qsrc + ((size_t)g * N + n0) * (K / 2), static_cast<uint32_t>(qrows * (K / 2)));
+      const __amdgpu_buffer_rsrc_t s_rsrc = buffer_rsrc(
+          ssrc + ((size_t)g * N + n0) * (K / 32), static_cast<uint32_t>(qrows * (K / 32)));
+      const uint32_t q_off = static_cast<uint32_t>(qlocal) * (K / 2) + qhalf * 16;
+      const uint32_t s_off = static_cast<uint32_t>(qlocal) * (K / 32) + qhalf;
+      u32x4 rq[2];
+      uint32_t rs[2];
+#define MOE_FETCHQ(kt, P)                                                               \
+  do {                                                                                  \
+    const uint32_t k0_ = (kt) * kRowBytes;                                              \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
+        ra[P][i] = load16(a_rsrc, a_off[i], k0_);                                       \
+    rq[P] = load16(q_rsrc, q_off, (kt) * 32);                                           \
+    rs[P] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_off, (kt) * 2, 0);            \
+  } while (0)
+#define MOE_STOREQ(kt, P)                                                               \
+  do {                                                                                  \
+    char* st_ = smem + ((kt) % kStages) * kStage;                                       \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
+        *reinterpret_cast<u32x4*>(st_ + lane * 16 + (2 * wv + i) * 1024) = ra[P][i];    \
+    const float sc_ = mx_scale(rs[P]);                                                  \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                       \
+        *reinterpret_cast<u32x4*>(st_ + kStageA + swz(qrow, 4 * qhalf + j)) =           \
+            mxfp4_chunk(rq[P][j], sc_);                                                 \
+  } while (0)
+#define MOE_STEPQ(kt, P, NEXT)                                                          \
+  do {                                                                                  \
+    MOE_FETCHQ(min((kt) + 2, KT - 1), P);                                               \
+    const char* st = smem + (P) * kStage;                                               \
+    _Pragma("unroll") for (int s = 0; s < S; ++s) {                                     \
+      const int cur = s & 1, nxt = cur ^ 1;                                             \
+      if (s + 1 < S) {                                                                  \
+        MOE_LOADF(st, s + 1, nxt);                                                      \
+      } else if (NEXT) {                                                                \
+        MOE_STOREQ((kt) + 1, (P) ^ 1);                                                  \
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                 \
+        MOE_LOADF(smem + ((P) ^ 1) * kStage, 0, nxt);                                   \
+      }                                                                                 \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      _Pragma("unroll") for (int ni = 0; ni < 2; ++ni) {                                \
+        acc[0][ni] = Mfma<TE>::mma(fa[cur][0], fb[cur][ni], acc[0][ni]);                \
+        acc[1][ni] = Mfma<TE>::mma(fa[cur][1], fb[cur][ni], acc[1][ni]);                \
+      }                                                                                 \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+    }                                                                                   \
+  } while (0)
+      MOE_FETCHQ(0, 0);
+      MOE_FETCHQ(1, 1);
+      MOE_STOREQ(0, 0);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      MOE_LOADF(smem, 0, 0);
+      int kt = 0;
+      for (; kt + 2 < KT; kt += 2) {
+        MOE_STEPQ(kt, 0, 1);
+        MOE_STEPQ(kt + 1, 1, 1);
+      }
+      MOE_STEPQ(kt, 0, 1);
+      MOE_STEPQ(kt + 1, 1, 0);
+#undef MOE_STEPQ
+#undef MOE_STOREQ
+#undef MOE_FETCHQ
+    } else {
     // KT is even: d and I are multiples of 256 and 128 elements, i.e. of 2 K steps.  The
     // last step (NEXT = 0) is peeled off the loop so that no control-flow join sits
     // between a fragment load and the MFMAs that do not depend on it (the waitcnt pass
@@ -310,6 +415,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
     }
     MOE_STEP(kt, 0, 1);
     MOE_STEP(kt + 1, 1, 0);
+    }
 #undef MOE_STEP
 #undef MOE_LOADF
 #undef MOE_STORE
@@ -699,15 +805,45 @@ static hipError_t launch_typed(const TE* x, const int32_t* offsets, const int32_
   }
   hipLaunchKernelGGL(plan_kernel<kBM>, dim3(1), dim3(1024), 0, stream, offsets, G, plan,
                      sync);
-  hipLaunchKernelGGL((grouped_gemm_kernel<TE, 0>), dim3(grid),
+  hipLaunchKernelGGL((grouped_gemm_kernel<TE, 0, false>), dim3(grid),
                      dim3(512), 0, stream, x, row_token, wg, wu, offsets, plan,
                      static_cast<void*>(h), static_cast<uint32_t>((size_t)T * d * sizeof(TE)),
-                     d, I, T, nt_gu, d, hp);
-  hipLaunchKernelGGL((grouped_gemm_kernel<TE, 1>), dim3(grid),
+                     d, I, T, nt_gu, d, hp, nullptr, nullptr, nullptr, nullptr, 0);
+  hipLaunchKernelGGL((grouped_gemm_kernel<TE, 1, false>), dim3(grid),
                      dim3(512), 0, stream, static_cast<const TE*>(h), row_token, wd, wd,
                      offsets, plan, static_cast<void*>(y),
                      static_cast<uint32_t>((size_t)R * hp * sizeof(TE)), I, d, T, nt_dn, hp,
-                     d);
+                     d, nullptr, nullptr, nullptr, nullptr, 0);
+  return hipGetLastError();
+}
+
+// bf16 layer whose E routed experts are MXFP4 (the S shared experts bf16 [S, ...]):
+// 128-row tiles for every workload.
+hipError_t launch_grouped_swiglu_mxfp4(const uint16_t* x, const int32_t* offsets,
+                                       const int32_t* row_token, const MxWeights& q,
+                                       const uint16_t* wg_shared, const uint16_t* wu_shared,
+                                       const uint16_t* wd_shared, uint16_t* h, float* y,
+                                       PlanEntry* plan, int T, int d, int I, int E, int G,
+                                       int R, hipStream_t stream) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const uint32_t grid = static_cast<uint32_t>(cus / kXcds > 0 ? cus / kXcds * kXcds : kXcds);
+  uint32_t* sync = reinterpret_cast<uint32_t*>(plan + 1 + max_mtiles(R, G));
+  const int hp = static_cast<int>(h_pitch(I));
+  hipLaunchKernelGGL(plan_kernel<kBM>, dim3(1), dim3(1024), 0, stream, offsets, G, plan,
+                     sync);
+  hipLaunchKernelGGL((grouped_gemm_kernel<uint16_t, 0, true>), dim3(grid), dim3(512), 0,
+                     stream, x, row_token, wg_shared, wu_shared, offsets, plan,
+                     static_cast<void*>(h), static_cast<uint32_t>((size_t)T * d * 2), d, I, T,
+                     I / kGateUpBN, d, hp, q.codes_gate, q.codes_up, q.scales_gate,
+                     q.scales_up, E);
+  hipLaunchKernelGGL((grouped_gemm_kernel<uint16_t, 1, true>), dim3(grid), dim3(512), 0,
+                     stream, static_cast<const uint16_t*>(h), row_token, wd_shared, wd_shared,
+                     offsets, plan, static_cast<void*>(y),
+                     static_cast<uint32_t>((size_t)R * hp * 2), I, d, T, d / kDownBN, hp, d,
+                     q.codes_down, q.codes_down, q.scales_down, q.scales_down, E);
   return hipGetLastError();
 }
 

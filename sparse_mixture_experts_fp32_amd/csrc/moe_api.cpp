@@ -189,6 +189,37 @@ moe_status_t do_grouped(const moe_config_t& c, int64_t T, const void* x,
                 stream);
 }
 
+moe_status_t do_grouped_mxfp4(const moe_config_t& c, int64_t T, const void* x,
+                              const int32_t* offsets, const int32_t* row_token,
+                              const moe::MxWeights& q, const void* wg_shared,
+                              const void* wu_shared, const void* wd_shared, float* y_rows,
+                              void* ws, hipStream_t stream) {
+  const Layout L = layout_of(c, T);
+  const Dims m = dims_of(c, T);
+  return finish(moe::launch_grouped_swiglu_mxfp4(
+                    static_cast<const uint16_t*>(x), offsets, row_token, q,
+                    static_cast<const uint16_t*>(wg_shared),
+                    static_cast<const uint16_t*>(wu_shared),
+                    static_cast<const uint16_t*>(wd_shared), at<uint16_t>(ws, L.h), y_rows,
+                    at<PlanEntry>(ws, L.plan), (int)m.T, (int)m.d, (int)m.I, (int)m.E,
+                    (int)m.G, (int)m.R, stream),
+                stream);
+}
+
+// MXFP4 pointers: codes 16-byte aligned; shared experts' bf16 weights present iff S > 0.
+moe_status_t check_mxfp4(const moe_config_t& c, const uint8_t* const* q, const void* wg_s,
+                         const void* wu_s, const void* wd_s) {
+  if (c.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  for (int i = 0; i < 6; ++i)
+    if (q[i] == nullptr) return MOE_ERR_ARG;
+  if (!aligned16(q[0]) || !aligned16(q[2]) || !aligned16(q[4])) return MOE_ERR_ARG;
+  if (c.n_shared > 0) {
+    if (wg_s == nullptr || wu_s == nullptr || wd_s == nullptr) return MOE_ERR_ARG;
+    if (!aligned16(wg_s) || !aligned16(wu_s) || !aligned16(wd_s)) return MOE_ERR_ARG;
+  }
+  return MOE_OK;
+}
+
 moe_status_t do_combine(const moe_config_t& c, int64_t T, const float* y_rows,
                         const int32_t* slot_row, const float* weights, const float* residual,
                         float* out, hipStream_t stream) {
@@ -312,6 +343,67 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x,
   MOE_TRY(do_route(*cfg, T, x, w_router, sel_bias, logit_offset, idx, wts, ws, stream));
   MOE_TRY(do_permute(*cfg, T, idx, counts, offsets, row_token, slot_row, ws, stream));
   MOE_TRY(do_grouped(*cfg, T, x, offsets, row_token, w_gate, w_up, w_down, y, ws, stream));
+  return do_combine(*cfg, T, y, slot_row, wts, residual, out, stream);
+}
+
+moe_status_t moe_grouped_swiglu_mxfp4(const moe_config_t* cfg, int64_t T, const void* x,
+                                      const int32_t* offsets, const int32_t* row_token,
+                                      const uint8_t* wq_gate, const uint8_t* ws_gate,
+                                      const uint8_t* wq_up, const uint8_t* ws_up,
+                                      const uint8_t* wq_down, const uint8_t* ws_down,
+                                      const void* w_gate_shared, const void* w_up_shared,
+                                      const void* w_down_shared, float* y_rows, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_tokens(*cfg, T));
+  const uint8_t* q[6] = {wq_gate, ws_gate, wq_up, ws_up, wq_down, ws_down};
+  MOE_TRY(check_mxfp4(*cfg, q, w_gate_shared, w_up_shared, w_down_shared));
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || offsets == nullptr || row_token == nullptr || y_rows == nullptr)
+    return MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(y_rows)) return MOE_ERR_ARG;
+  MOE_TRY(check_ws(*cfg, T, ws, ws_bytes));
+  (void)hipGetLastError();
+  const moe::MxWeights mx{wq_gate, ws_gate, wq_up, ws_up, wq_down, ws_down};
+  return do_grouped_mxfp4(*cfg, T, x, offsets, row_token, mx, w_gate_shared, w_up_shared,
+                          w_down_shared, y_rows, ws, stream);
+}
+
+moe_status_t moe_forward_mxfp4(const moe_config_t* cfg, int64_t T, const void* x,
+                               const void* w_router, const float* sel_bias,
+                               const float* logit_offset, const uint8_t* wq_gate,
+                               const uint8_t* ws_gate, const uint8_t* wq_up,
+                               const uint8_t* ws_up, const uint8_t* wq_down,
+                               const uint8_t* ws_down, const void* w_gate_shared,
+                               const void* w_up_shared, const void* w_down_shared,
+                               const float* residual, float* out, int32_t* topk_idx_out,
+                               int32_t* counts_out, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_tokens(*cfg, T));
+  const uint8_t* q[6] = {wq_gate, ws_gate, wq_up, ws_up, wq_down, ws_down};
+  MOE_TRY(check_mxfp4(*cfg, q, w_gate_shared, w_up_shared, w_down_shared));
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || w_router == nullptr || out == nullptr) return MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(out) ||
+      (residual != nullptr && !aligned16(residual)))
+    return MOE_ERR_ARG;
+  if (sel_bias != nullptr && cfg->router != MOE_ROUTER_SIGMOID_SHARED) return MOE_ERR_ARG;
+  MOE_TRY(check_ws(*cfg, T, ws, ws_bytes));
+  (void)hipGetLastError();
+  const Layout L = layout_of(*cfg, T);
+  int32_t* idx = topk_idx_out != nullptr ? topk_idx_out : at<int32_t>(ws, L.idx);
+  int32_t* counts = counts_out != nullptr ? counts_out : at<int32_t>(ws, L.counts);
+  float* wts = at<float>(ws, L.wts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  int32_t* slot_row = at<int32_t>(ws, L.slot_row);
+  float* y = at<float>(ws, L.y);
+  const moe::MxWeights mx{wq_gate, ws_gate, wq_up, ws_up, wq_down, ws_down};
+  MOE_TRY(do_route(*cfg, T, x, w_router, sel_bias, logit_offset, idx, wts, ws, stream));
+  MOE_TRY(do_permute(*cfg, T, idx, counts, offsets, row_token, slot_row, ws, stream));
+  MOE_TRY(do_grouped_mxfp4(*cfg, T, x, offsets, row_token, mx, w_gate_shared, w_up_shared,
+                           w_down_shared, y, ws, stream));
   return do_combine(*cfg, T, y, slot_row, wts, residual, out, stream);
 }
 

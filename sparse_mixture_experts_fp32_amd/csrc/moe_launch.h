@@ -47,6 +47,20 @@ hipError_t launch_grouped_swiglu(int dtype, const void* x, const int32_t* offset
                                  float* y_rows, PlanEntry* plan, int T, int d, int I, int G,
                                  int R, hipStream_t stream);
 
+// MXFP4 routed-expert weights: codes [E, N, K/2] (element 2i in the low nibble) and E8M0
+// scales [E, N, K/32] per tensor (gate/up: N = I, K = d; down: N = d, K = I).
+struct MxWeights {
+  const uint8_t *codes_gate, *scales_gate, *codes_up, *scales_up, *codes_down, *scales_down;
+};
+
+// Grouped SwiGLU with MXFP4 routed experts and bf16 shared experts ([S, ...]); bf16 x.
+hipError_t launch_grouped_swiglu_mxfp4(const uint16_t* x, const int32_t* offsets,
+                                       const int32_t* row_token, const MxWeights& q,
+                                       const uint16_t* wg_shared, const uint16_t* wu_shared,
+                                       const uint16_t* wd_shared, uint16_t* h, float* y,
+                                       PlanEntry* plan, int T, int d, int I, int E, int G,
+                                       int R, hipStream_t stream);
+
 // Weighted combine of each token's A = k + S rows, fixed order, optional residual.
 hipError_t launch_combine(const float* y_rows, const int32_t* slot_row, const float* weights,
                           const float* residual, float* out, int T, int d, int A, int R,

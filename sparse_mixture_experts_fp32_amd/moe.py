@@ -48,6 +48,7 @@ def make_config(d_model, n_experts, d_ff, top_k, n_shared, router, dtype,
 
 
 _lib = None
+ARGTYPES: dict = {}   # entry point -> number of C parameters bound (set by load_library)
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -77,15 +78,31 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_combine": [CFG, I64, P, P, P, P, P, P],
         "moe_forward": [CFG, I64, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_rmsnorm": [CFG, I64, P, P, ctypes.c_float, ctypes.c_int32, P, P],
+        "moe_grouped_swiglu_mxfp4": [CFG, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ,
+                                     P],
+        "moe_forward_mxfp4": [CFG, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                              SZ, P],
         "moe_forward_rmsnorm": [CFG, I64, P, P, ctypes.c_float, ctypes.c_int32, P, P, P, P,
                                 P, P, P, P, P, P, P, SZ, P],
     }
+    global ARGTYPES
+    ARGTYPES = {name: len(args) for name, args in sigs.items()}
     for name, args in sigs.items():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+def header_param_counts(path: str = HEADER_PATH) -> dict:
+    """Number of parameters of each function include/moe.h declares."""
+    src = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"(moe_\w+)\s*\(([^;{]*?)\)\s*;", src, re.S):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
 
 
 def header_functions(path: str = HEADER_PATH) -> list[str]:
@@ -177,3 +194,24 @@ def moe_forward_rmsnorm(cfg, T, x, norm_gain, eps, zero_centred, w_router, sel_b
         _ptr(w_router), _ptr(sel_bias), _ptr(logit_offset), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(residual), _ptr(out), _ptr(topk_idx_out), _ptr(counts_out),
         _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_grouped_swiglu_mxfp4(cfg, T, x, offsets, row_token, wq_gate, ws_gate, wq_up, ws_up,
+                             wq_down, ws_down, w_gate_shared, w_up_shared, w_down_shared,
+                             y_rows, ws, ws_bytes, stream=None):
+    _check(load_library().moe_grouped_swiglu_mxfp4(
+        ctypes.byref(cfg), T, _ptr(x), _ptr(offsets), _ptr(row_token), _ptr(wq_gate),
+        _ptr(ws_gate), _ptr(wq_up), _ptr(ws_up), _ptr(wq_down), _ptr(ws_down),
+        _ptr(w_gate_shared), _ptr(w_up_shared), _ptr(w_down_shared), _ptr(y_rows),
+        _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_forward_mxfp4(cfg, T, x, w_router, sel_bias, logit_offset, wq_gate, ws_gate, wq_up,
+                      ws_up, wq_down, ws_down, w_gate_shared, w_up_shared, w_down_shared,
+                      residual, out, topk_idx_out, counts_out, ws, ws_bytes, stream=None):
+    _check(load_library().moe_forward_mxfp4(
+        ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(sel_bias), _ptr(logit_offset),
+        _ptr(wq_gate), _ptr(ws_gate), _ptr(wq_up), _ptr(ws_up), _ptr(wq_down), _ptr(ws_down),
+        _ptr(w_gate_shared), _ptr(w_up_shared), _ptr(w_down_shared), _ptr(residual),
+        _ptr(out), _ptr(topk_idx_out), _ptr(counts_out), _ptr(ws), ws_bytes,
+        _stream(stream)))

@@ -49,6 +49,13 @@ def workspace(cfg, T, torch):
     return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda"), n
 
 
+def shared_weights(c, dev: dict):
+    """The shared experts' dense weights of an MXFP4 workload (None when S = 0)."""
+    if c.S == 0:
+        return (None, None, None)
+    return (dev["w_gate"], dev["w_up"], dev["w_down"])
+
+
 def run_forward(c, dev: dict, torch, residual=None, ws=None):
     """moe_forward (moe_forward_rmsnorm for pre-norm workloads, whose x is the raw hidden
     state) on device tensors; returns (out, topk_idx, counts) device tensors."""
@@ -60,7 +67,13 @@ def run_forward(c, dev: dict, torch, residual=None, ws=None):
     out = torch.empty((T, c.d), dtype=torch.float32, device="cuda")
     idx = torch.empty((T, c.k), dtype=torch.int32, device="cuda")
     counts = torch.empty((c.E + c.S,), dtype=torch.int32, device="cuda")
-    if c.prenorm:
+    if c.weight_format == "mxfp4":
+        sh = shared_weights(c, dev)
+        M.moe_forward_mxfp4(cfg, T, dev["x"], dev["w_router"], dev.get("sel_bias"),
+                            dev.get("logit_offset"), dev["wq_gate"], dev["ws_gate"],
+                            dev["wq_up"], dev["ws_up"], dev["wq_down"], dev["ws_down"], *sh,
+                            residual, out, idx, counts, buf, n)
+    elif c.prenorm:
         M.moe_forward_rmsnorm(cfg, T, dev["x"], dev["norm_gain"], c.norm_eps,
                               c.norm_zero_centred, dev["w_router"], dev.get("sel_bias"),
                               dev.get("logit_offset"), dev["w_gate"], dev["w_up"],
@@ -134,8 +147,15 @@ class StagedRunner:
                       self.slot_row, self.ws, self.nws, stream)
         if ev is not None:
             ev[2].record(stream)
-        M.moe_grouped_swiglu(cfg, T, x, self.offsets, self.row_token, d["w_gate"],
-                             d["w_up"], d["w_down"], self.y_rows, self.ws, self.nws, stream)
+        if c.weight_format == "mxfp4":
+            M.moe_grouped_swiglu_mxfp4(cfg, T, x, self.offsets, self.row_token,
+                                       d["wq_gate"], d["ws_gate"], d["wq_up"], d["ws_up"],
+                                       d["wq_down"], d["ws_down"], *shared_weights(c, d),
+                                       self.y_rows, self.ws, self.nws, stream)
+        else:
+            M.moe_grouped_swiglu(cfg, T, x, self.offsets, self.row_token, d["w_gate"],
+                                 d["w_up"], d["w_down"], self.y_rows, self.ws, self.nws,
+                                 stream)
         if ev is not None:
             ev[3].record(stream)
         M.moe_combine(cfg, T, self.y_rows, self.slot_row, self.w, residual, self.out, stream)

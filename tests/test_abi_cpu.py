@@ -24,12 +24,25 @@ def cfg_of(c, **kw):
     return M.make_config(**args)
 
 
+def test_binding_parameter_counts_match_the_header():
+    from sparse_mixture_experts_fp32_amd import moe as binding
+    binding.load_library()
+    counts = binding.header_param_counts()
+    bound = binding.ARGTYPES
+    assert set(bound) <= set(counts)
+    for name, n in bound.items():
+        assert counts[name] == n, (name, counts[name], n)
+    # every declared entry point is bound
+    assert set(counts) - set(bound) == {"moe_status_str"}
+
+
 def test_library_exports_every_declared_function():
     lib = M.load_library()
     names = M.header_functions()
     assert set(names) == {"moe_status_str", "moe_workspace_size", "moe_route", "moe_permute",
                           "moe_grouped_swiglu", "moe_combine", "moe_forward", "moe_rmsnorm",
-                          "moe_forward_rmsnorm"}
+                          "moe_forward_rmsnorm", "moe_grouped_swiglu_mxfp4",
+                          "moe_forward_mxfp4"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -146,6 +159,30 @@ def test_rmsnorm_entry_points_validate_before_launch():
                   A, None, A, None, None, A, need) == M.MOE_ERR_ARG
     # T = 0 is a no-op
     M.moe_rmsnorm(cfg, 0, None, None, 1e-6, 0, None, stream=0)
+
+
+def test_mxfp4_entry_points_validate_before_launch():
+    c = CONFIGS["inkling_decode"]
+    cfg = cfg_of(c)
+    need = M.moe_workspace_size(cfg, c.T)
+    q = [A, A + 1, A, A + 1, A, A + 1]          # codes aligned, scales any byte address
+
+    def status(fn, *args):
+        with pytest.raises(M.MoEError) as ei:
+            fn(*args, stream=0)
+        return ei.value.status
+
+    f32 = cfg_of(c, dtype="f32")
+    assert status(M.moe_grouped_swiglu_mxfp4, f32, c.T, A, A, A, *q, A, A, A, A, A,
+                  need) == M.MOE_ERR_UNSUPPORTED
+    assert status(M.moe_grouped_swiglu_mxfp4, cfg, c.T, A, A, A, None, *q[1:], A, A, A, A,
+                  A, need) == M.MOE_ERR_ARG
+    assert status(M.moe_grouped_swiglu_mxfp4, cfg, c.T, A, A, A, A + 8, *q[1:], A, A, A,
+                  A, A, need) == M.MOE_ERR_ARG                  # misaligned codes
+    assert status(M.moe_grouped_swiglu_mxfp4, cfg, c.T, A, A, A, *q, None, A, A, A, A,
+                  need) == M.MOE_ERR_ARG                        # S = 2 needs shared weights
+    assert status(M.moe_forward_mxfp4, cfg, c.T, A, A, None, None, *q, A, A, A, None, A,
+                  None, None, A, need - 1) == M.MOE_ERR_WORKSPACE
 
 
 def test_zero_tokens_is_a_no_op():

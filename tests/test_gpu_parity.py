@@ -80,6 +80,15 @@ PRENORM = {c.name: c for c in [
 # Widest supported RMSNorm row (RMSNorm stage only).
 NORM_WIDE = small("norm_wide", "sigmoid", "bf16", T=64, d=16384, E=8, S=0, I=128, k=2,
                   seed=28).with_(prenorm=True, norm_zero_centred=True)
+# MXFP4 routed experts (bf16 shared experts), 128-row tiles.
+MXFP4 = {c.name: c for c in [
+    small("mx_sig_decode", "sigmoid", "bf16", T=32, d=512, E=40, S=2, I=256, k=6,
+          seed=29).with_(weight_format="mxfp4"),
+    small("mx_sig_rows", "sigmoid", "bf16", T=400, d=256, E=6, S=1, I=256, k=2,
+          seed=30).with_(weight_format="mxfp4"),
+    small("mx_soft", "softmax", "bf16", T=100, d=512, E=12, S=0, I=128, k=3,
+          seed=31).with_(weight_format="mxfp4"),
+]}
 # A one-ulp difference of a bf16 normalized input (f32 statistic on the GPU, float64 in
 # the oracle) moves a logit by up to ~1e-4; near-ties below this are excluded on pre-norm
 # paths (and must still be valid alternatives).
@@ -158,6 +167,25 @@ def test_forward_rmsnorm(name):
     excl = check_routing(idx, ref.routing, c.E, gap=PRENORM_GAP)
     assert (counts[:c.E] == np.bincount(idx.ravel(), minlength=c.E)).all()
     mx, mn = assert_outputs(out[~excl], ref.y[~excl], f"{name} forward_rmsnorm")
+    log(f"{name}: excluded {excl.sum()}/{c.T}, max rel {mx:.2e}, mean rel {mn:.2e}")
+
+
+@pytest.mark.parametrize("name", list(MXFP4))
+def test_forward_mxfp4(name):
+    """moe_forward_mxfp4 against the oracle on the dequantized routed experts; the staged
+    sequence must match it bit for bit."""
+    c = MXFP4[name]
+    inp, dev = inputs_of(c)
+    out, idx, counts = run_forward(c, dev, torch)
+    run = StagedRunner(c, dev, torch)
+    run.step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(out, run.out) and torch.equal(idx, run.idx)
+    out, idx, counts = out.cpu().numpy(), idx.cpu().numpy(), counts.cpu().numpy()
+    ref = O.moe_forward(c, inp, mode=mode_of(c))
+    excl = check_routing(idx, ref.routing, c.E)
+    assert (counts[:c.E] == np.bincount(idx.ravel(), minlength=c.E)).all()
+    mx, mn = assert_outputs(out[~excl], ref.y[~excl], f"{name} forward_mxfp4")
     log(f"{name}: excluded {excl.sum()}/{c.T}, max rel {mx:.2e}, mean rel {mn:.2e}")
 
 
@@ -286,7 +314,8 @@ def test_zero_router_tie_rule_on_gpu():
 
 # ------------------------------------------------------------------------ full size
 FULL_SAMPLE = {"inkling_decode": None, "inkling_prefill": 48, "qwen38": 24,
-               "inkling_skewed": 48, "qwen38_shared": 24, "kimi_k3_latent": 48}
+               "inkling_skewed": 48, "qwen38_shared": 24, "kimi_k3_latent": 48,
+               "inkling_decode_mxfp4": None}
 
 
 @pytest.mark.parametrize("name", list(FULL_SAMPLE))
