@@ -74,28 +74,23 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t
 // and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// MXFP4 (OCP Microscaling FP4) decode.  E8M0 scale byte s -> 2^(s - 127) (s = 0 is the
-// f32 subnormal 2^-127, s = 255 NaN).  E2M1 code c: sign bit 3, exponent bits 2..1 (bias
-// 1), mantissa bit 0; exponent 0 is subnormal (0 or 0.5).
-__device__ __forceinline__ float mx_scale(uint32_t s) {
-  s &= 0xffu;
-  return __uint_as_float(s == 0 ? 0x00400000u : (s == 255 ? 0x7fc00000u : s << 23));
-}
-__device__ __forceinline__ float e2m1_f32(uint32_t c) {
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  const uint32_t mag = e ? ((126u + e) << 23) | (m << 22) : (m ? 0x3f000000u : 0u);
-  return __uint_as_float(mag | ((c & 8u) << 28));
-}
+// MXFP4 (OCP Microscaling FP4) decode with gfx950's scaled conversion: one
+// v_cvt_scalef32_pk_bf16_fp4 turns the two E2M1 codes of one byte (element 0 in the low
+// nibble) into two bf16, multiplied by 2^(exponent field of the f32 scale operand - 127)
+// and rounded to nearest even.  Only the scale's exponent field is read, so the E8M0 byte
+// s is passed as the f32 bit pattern s << 23: s = 0 gives 2^-127 and s = 255 a NaN, as
+// the E8M0 format defines.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float mx_scale(uint32_t s) { return __uint_as_float((s & 0xffu) << 23); }
 // 8 codes (one 32-bit word, element i in bits 4i..4i+3) -> 8 bf16 (one 16-byte chunk,
 // element i in halfword i).
 __device__ __forceinline__ u32x4 mxfp4_chunk(uint32_t w, float sc) {
   u32x4 o;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t lo = f32_to_bf16_rne(e2m1_f32((w >> (8 * p)) & 15u) * sc);
-    const uint32_t hi = f32_to_bf16_rne(e2m1_f32((w >> (8 * p + 4)) & 15u) * sc);
-    o[p] = lo | (hi << 16);
-  }
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
   return o;
 }
 
@@ -448,6 +443,262 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
   }
 }
 
+// ---- Decode-shaped tiles (bf16 layers with at most 32 tokens)
+//
+// Every group then has at most 32 rows, so one 32-row m-tile per group, and the step is
+// bound by streaming the experts' weights.  A tile is 32 rows x 128 B-rows (gate/up: 64
+// gate + 64 up rows of the same h columns; down: 128 output columns); the 4 waves of a
+// workgroup split its K range into interleaved chunks and each wave loads its A rows and
+// B-rows straight from memory into registers in the MFMA operand layout, double-buffered
+// a chunk ahead, so the K loop has no LDS traffic and no barrier.  The K order inside a
+// chunk is permuted (the product sums over K, so any order shared by A and B is exact) so
+// that each load reads 16 contiguous bytes of a row and, for an MXFP4 B-row, one load is
+// one MX block (16 bytes of codes, one scale byte).  MXFP4 codes are converted to bf16 in
+// registers.  Rows past the group's end load a copy of its last row (their outputs are
+// not stored).  The 4 waves' partial 32 x 128 sums are added in LDS in wave order, then
+// the SwiGLU (gate/up) or the f32 row store (down) runs.  Tiles are taken from a
+// counter, last plan m-tile first, so the shared experts' bf16 tiles (about 4x the bytes
+// of an MXFP4 tile) start before the routed ones.
+constexpr int kSkBM = 32;                 // rows per m-tile
+constexpr int kSkWaves = 4;               // waves per workgroup (K split)
+constexpr int kSkBlocks = 4;              // 32-wide B-row blocks per tile (128 B-rows)
+
+template <int MODE, bool FP4>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void grouped_gemm_skinny_kernel(
+    const uint16_t* __restrict__ a_src,      // MODE 0: x [T, K]; MODE 1: h [R, K] (pitch lda)
+    const int32_t* __restrict__ row_token,   // MODE 0 only
+    const uint16_t* __restrict__ b0,         // bf16 B: MODE 0 gate, MODE 1 down [., N, K]
+    const uint16_t* __restrict__ b1,         // bf16 B: MODE 0 up
+    const uint8_t* __restrict__ q0, const uint8_t* __restrict__ q1,   // MXFP4 codes
+    const uint8_t* __restrict__ s0, const uint8_t* __restrict__ s1,   // E8M0 scales
+    const PlanEntry* __restrict__ plan, uint32_t* __restrict__ next_tile,
+    void* __restrict__ c_out, uint32_t a_bytes, int K, int N, int T, int NT, int lda,
+    int ldc, int E) {
+  // FP4: groups g < E are MXFP4 (codes [E, N, K/2], scales [E, N, K/32]) and groups
+  // g >= E bf16 at index g - E of b0 / b1; otherwise every group is bf16 at index g.
+  __shared__ float red[kSkWaves * kSkBlocks * 16 * 64];   // 64 KB of partial sums
+  __shared__ uint32_t s_tile;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, lh = lane >> 5;
+  const uint32_t ntiles = static_cast<uint32_t>(plan[0].group) * NT;
+  const __amdgpu_buffer_rsrc_t a_rsrc = buffer_rsrc(a_src, a_bytes);
+  constexpr int kRowsPerSrc = MODE == 0 ? 64 : 128;   // B-rows of one source per tile
+
+  for (;;) {
+    if (tid == 0) s_tile = atomicAdd(next_tile, 1u);
+    __syncthreads();
+    const uint32_t t = __builtin_amdgcn_readfirstlane(s_tile);
+    if (t >= ntiles) break;
+    const uint32_t logical = ntiles - 1 - t;
+    const PlanEntry pe = plan[1 + logical / NT];
+    const int g = pe.group, row0 = pe.row0, nrows = pe.nrows;
+    const int n0 = static_cast<int>(logical % NT) * kRowsPerSrc;
+    const bool quant = FP4 && g < E;
+
+    // A row of this lane; lanes past the group's rows read its last row (an MFMA output
+    // row depends only on its own A row, and those rows are not stored).
+    uint32_t a_row;
+    {
+      const int lr_ = min(ln, nrows - 1);
+      if (MODE == 0) {
+        int tok = row_token[row0 + lr_];
+        tok = min(max(tok, 0), T - 1);
+        a_row = static_cast<uint32_t>(tok) * lda * 2;
+      } else {
+        a_row = static_cast<uint32_t>(row0 + lr_) * lda * 2;
+      }
+    }
+    // B-row of this lane in block b, relative to its source's tile base: ln + bro(b).
+    // Gate/up blocks 0, 1 are gate rows and 2, 3 the up rows of the same columns.
+#define MOE_SK_BRO(b) (MODE == 0 ? 32 * ((b) & 1) : 32 * (b))
+
+    f32x16 acc[kSkBlocks];
+#pragma unroll
+    for (int b = 0; b < kSkBlocks; ++b) acc[b] = f32x16{};
+
+    if (quant) {
+      // MXFP4 B: chunks of 128 K elements (64 code bytes and 4 scale bytes per B-row).
+      // Wave w takes the chunk pairs 8 p + 2 w, 8 p + 2 w + 1 (one 128-byte line of codes
+      // and 8 scale bytes per B-row); iteration i of a wave is chunk 8 (i / 2) + 2 w + i % 2.
+      // Load j of a chunk gives lane half hh of B-row n the code bytes 32 j + 16 hh .. +16,
+      // i.e. MX block 2 j + hh of the chunk; MFMA step (j, u) covers K elements
+      // 64 j + 32 hh + 8 u .. +8 of the chunk for A and B alike.
+      const int nch = K / 128;
+      const int nw = 2 * ((nch + 2 * kSkWaves - 1) / (2 * kSkWaves));
+      const size_t qbase = ((size_t)g * N + n0) * (K / 2);
+      const size_t sbase = ((size_t)g * N + n0) * (K / 32);
+      const uint32_t qbytes = static_cast<uint32_t>(kRowsPerSrc * (K / 2));
+      const uint32_t sbytes = static_cast<uint32_t>(kRowsPerSrc * (K / 32));
+      const __amdgpu_buffer_rsrc_t qr0 = buffer_rsrc(q0 + qbase, qbytes);
+      const __amdgpu_buffer_rsrc_t qr1 = buffer_rsrc((MODE == 0 ? q1 : q0) + qbase, qbytes);
+      const __amdgpu_buffer_rsrc_t sr0 = buffer_rsrc(s0 + sbase, sbytes);
+      const __amdgpu_buffer_rsrc_t sr1 = buffer_rsrc((MODE == 0 ? s1 : s0) + sbase, sbytes);
+      const uint32_t a_voff = a_row + 64 * lh;
+      // Per-block vector offsets (the block's row offset as a scalar offset was slower).
+      uint32_t q_voff[kSkBlocks];
+#pragma unroll
+      for (int b = 0; b < kSkBlocks; ++b)
+        q_voff[b] = static_cast<uint32_t>(ln + MOE_SK_BRO(b)) * (K / 2) + 16 * lh;
+      const uint32_t s_voff = static_cast<uint32_t>(ln) * (K / 32);
+      u32x4 ra[2][8], rq[2][kSkBlocks][2];
+      u32x2 rsp[kSkBlocks];          // scale bytes of the current pair
+      uint32_t rs_hi[kSkBlocks];     // the pair's second chunk, kept past the next fetch
+#define MOE_SKQ_CHUNK(i) (8 * ((i) >> 1) + 2 * wv + ((i) & 1))
+#define MOE_SKQ_FETCH(i, P)                                                             \
+  do {                                                                                  \
+    const uint32_t c_ = static_cast<uint32_t>(min(MOE_SKQ_CHUNK(i), nch - 1));          \
+    _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                             \
+      const __amdgpu_buffer_rsrc_t qr_ = (MODE == 0 && b >= 2) ? qr1 : qr0;             \
+      const uint32_t qo_ = c_ * 64;                                                     \
+      rq[P][b][0] = load16(qr_, q_voff[b], qo_);                                        \
+      rq[P][b][1] = load16(qr_, q_voff[b], qo_ + 32);                                   \
+      if ((P) == 0)                                                                     \
+        rsp[b] = __builtin_amdgcn_raw_buffer_load_b64((MODE == 0 && b >= 2) ? sr1 : sr0, \
+                                                      s_voff,                           \
+                                                      MOE_SK_BRO(b) * (K / 32) + c_ * 4, 0); \
+    }                                                                                   \
+    _Pragma("unroll") for (int u = 0; u < 8; ++u)                                       \
+        ra[P][u] = load16(a_rsrc, a_voff, c_ * 256 + 128 * (u >> 2) + 16 * (u & 3));    \
+  } while (0)
+#define MOE_SKQ_MMA(i, P)                                                               \
+  do {                                                                                  \
+    if (MOE_SKQ_CHUNK(i) < nch) {                                                       \
+      uint32_t sw_[kSkBlocks];                                                          \
+      _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                           \
+        if ((P) == 0) {                                                                 \
+          sw_[b] = rsp[b][0];                                                           \
+          rs_hi[b] = rsp[b][1];                                                         \
+        } else {                                                                        \
+          sw_[b] = rs_hi[b];                                                            \
+        }                                                                               \
+      }                                                                                 \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                   \
+        float sc_[kSkBlocks];                                                           \
+        _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                           \
+            sc_[b] = mx_scale(sw_[b] >> (8 * (2 * j + lh)));                            \
+        _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                 \
+          const bf16x8 fa_ = __builtin_bit_cast(bf16x8, ra[P][4 * j + u]);              \
+          _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                       \
+            const bf16x8 fb_ =                                                          \
+                __builtin_bit_cast(bf16x8, mxfp4_chunk(rq[P][b][j][u], sc_[b]));        \
+            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_, fb_, acc[b], 0, 0, 0);\
+          }                                                                             \
+        }                                                                               \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
+      MOE_SKQ_FETCH(0, 0);
+      int i = 0;
+      for (; i + 2 < nw; i += 2) {
+        MOE_SKQ_FETCH(i + 1, 1);
+        MOE_SKQ_MMA(i, 0);
+        MOE_SKQ_FETCH(i + 2, 0);
+        MOE_SKQ_MMA(i + 1, 1);
+      }
+      MOE_SKQ_FETCH(i + 1, 1);
+      MOE_SKQ_MMA(i, 0);
+      MOE_SKQ_MMA(i + 1, 1);
+#undef MOE_SKQ_MMA
+#undef MOE_SKQ_FETCH
+#undef MOE_SKQ_CHUNK
+    } else {
+      // bf16 B: chunks of 64 K elements (128 bytes per B-row), wave w: chunks w, w + 4,
+      // ...  MFMA step u, operand half hh covers K elements 32 hh + 8 u .. +8 of the
+      // chunk, so each load reads 16 bytes of both 64-byte halves of the rows' lines.
+      const int gb = FP4 ? g - E : g;
+      const int nch = K / 64;
+      const int nw = max(2, ((nch + kSkWaves - 1) / kSkWaves + 1) & ~1);
+      const size_t bbase = ((size_t)gb * N + n0) * K;
+      const uint32_t bbytes = static_cast<uint32_t>(kRowsPerSrc * K * 2);
+      const __amdgpu_buffer_rsrc_t br0 = buffer_rsrc(b0 + bbase, bbytes);
+      const __amdgpu_buffer_rsrc_t br1 = buffer_rsrc((MODE == 0 ? b1 : b0) + bbase, bbytes);
+      const uint32_t a_voff = a_row + 64 * lh;
+      uint32_t b_voff[kSkBlocks];
+#pragma unroll
+      for (int b = 0; b < kSkBlocks; ++b)
+        b_voff[b] = static_cast<uint32_t>(ln + MOE_SK_BRO(b)) * K * 2 + 64 * lh;
+      u32x4 ra[2][4], rb[2][kSkBlocks][4];
+#define MOE_SKB_FETCH(i, P)                                                             \
+  do {                                                                                  \
+    const uint32_t c_ = static_cast<uint32_t>(min(wv + kSkWaves * (i), nch - 1));       \
+    _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                             \
+      const __amdgpu_buffer_rsrc_t br_ = (MODE == 0 && b >= 2) ? br1 : br0;             \
+      _Pragma("unroll") for (int u = 0; u < 4; ++u)                                     \
+          rb[P][b][u] = load16(br_, b_voff[b], c_ * 128 + 16 * u);                      \
+    }                                                                                   \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u)                                       \
+        ra[P][u] = load16(a_rsrc, a_voff, c_ * 128 + 16 * u);                           \
+  } while (0)
+#define MOE_SKB_MMA(i, P)                                                               \
+  do {                                                                                  \
+    if (wv + kSkWaves * (i) < nch) {                                                    \
+      _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                   \
+        const bf16x8 fa_ = __builtin_bit_cast(bf16x8, ra[P][u]);                        \
+        _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                           \
+            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                           \
+                fa_, __builtin_bit_cast(bf16x8, rb[P][b][u]), acc[b], 0, 0, 0);         \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
+      MOE_SKB_FETCH(0, 0);
+      int i = 0;
+      for (; i + 2 < nw; i += 2) {
+        MOE_SKB_FETCH(i + 1, 1);
+        MOE_SKB_MMA(i, 0);
+        MOE_SKB_FETCH(i + 2, 0);
+        MOE_SKB_MMA(i + 1, 1);
+      }
+      MOE_SKB_FETCH(i + 1, 1);
+      MOE_SKB_MMA(i, 0);
+      MOE_SKB_MMA(i + 1, 1);
+#undef MOE_SKB_MMA
+#undef MOE_SKB_FETCH
+    }
+#undef MOE_SK_BRO
+
+    // Partial sums -> LDS ([wave][block][register][lane]), then each wave adds the four
+    // waves' partials of its share in wave order.  Accumulator layout: lane l, register
+    // r -> B-row (l % 32), row 8 (r / 4) + 4 (l / 32) + (r % 4).
+    float* mine = red + wv * (kSkBlocks * 16 * 64);
+#pragma unroll
+    for (int b = 0; b < kSkBlocks; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mine[(b * 16 + r) * 64 + lane] = acc[b][r];
+    __syncthreads();
+    if (MODE == 0) {
+      // Wave w: h columns of block w % 2 (gate block w % 2, up block w % 2 + 2),
+      // registers 8 (w / 2) .. +8.
+      uint16_t* h = static_cast<uint16_t*>(c_out);
+      const int qb = wv & 1, r0 = 8 * (wv >> 1);
+#pragma unroll
+      for (int r = r0; r < r0 + 8; ++r) {
+        float gs = 0.0f, us = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < kSkWaves; ++w2) {
+          gs += red[((w2 * kSkBlocks + qb) * 16 + r) * 64 + lane];
+          us += red[((w2 * kSkBlocks + qb + 2) * 16 + r) * 64 + lane];
+        }
+        const int m = 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (m < nrows)
+          store_h(h + (size_t)(row0 + m) * ldc + n0 + 32 * qb + ln, silu(gs) * us);
+      }
+    } else {
+      float* y = static_cast<float*>(c_out);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float ys = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < kSkWaves; ++w2) ys += red[((w2 * kSkBlocks + wv) * 16 + r) * 64 + lane];
+        const int m = 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (m < nrows) y[(size_t)(row0 + m) * ldc + n0 + 32 * wv + ln] = ys;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ---- 256 x 256 tiles (bf16 layers whose groups average at least 128 rows)
 //
 // Same decomposition and plan as above with 256-row m-tiles.  A 256 x 256 tile moves
@@ -770,6 +1021,35 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   }
 }
 
+// Decode-shaped tiling: plan of 32-row m-tiles, then the gate/up and down kernels, each
+// taking tiles from its own counter (zeroed by the plan kernel).  Two workgroups per CU.
+template <bool FP4>
+static hipError_t launch_skinny(const uint16_t* x, const int32_t* offsets,
+                                const int32_t* row_token, const uint16_t* wg,
+                                const uint16_t* wu, const uint16_t* wd, const MxWeights& q,
+                                uint16_t* h, float* y, PlanEntry* plan, int T, int d, int I,
+                                int E, int G, int R, hipStream_t stream) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const uint32_t grid = static_cast<uint32_t>(2 * (cus > 0 ? cus : 256));
+  uint32_t* sync = reinterpret_cast<uint32_t*>(plan + 1 + max_mtiles(R, G));
+  const int hp = static_cast<int>(h_pitch(I));
+  hipLaunchKernelGGL(plan_kernel<kSkBM>, dim3(1), dim3(1024), 0, stream, offsets, G, plan,
+                     sync);
+  hipLaunchKernelGGL((grouped_gemm_skinny_kernel<0, FP4>), dim3(grid), dim3(256), 0, stream,
+                     x, row_token, wg, wu, q.codes_gate, q.codes_up, q.scales_gate,
+                     q.scales_up, plan, sync, static_cast<void*>(h),
+                     static_cast<uint32_t>((size_t)T * d * 2), d, I, T, I / 64, d, hp, E);
+  hipLaunchKernelGGL((grouped_gemm_skinny_kernel<1, FP4>), dim3(grid), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(h), row_token, wd, wd, q.codes_down,
+                     q.codes_down, q.scales_down, q.scales_down, plan, sync + 1,
+                     static_cast<void*>(y), static_cast<uint32_t>((size_t)R * hp * 2), I, d,
+                     T, d / 128, hp, d, E);
+  return hipGetLastError();
+}
+
 template <typename TE>
 static hipError_t launch_typed(const TE* x, const int32_t* offsets, const int32_t* row_token,
                                const TE* wg, const TE* wu, const TE* wd, TE* h, float* y,
@@ -781,6 +1061,11 @@ static hipError_t launch_typed(const TE* x, const int32_t* offsets, const int32_
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   const uint32_t grid = static_cast<uint32_t>(cus / kXcds > 0 ? cus / kXcds * kXcds : kXcds);
+  if constexpr (sizeof(TE) == 2) {
+    if (T <= kDecodeMaxTokens)
+      return launch_skinny<false>(x, offsets, row_token, wg, wu, wd, MxWeights{}, h, y, plan,
+                                  T, d, I, G, G, R, stream);
+  }
   const int nt_gu = I / kGateUpBN;
   const int nt_dn = d / kDownBN;
   uint32_t* sync = reinterpret_cast<uint32_t*>(plan + 1 + max_mtiles(R, G));
@@ -825,6 +1110,9 @@ hipError_t launch_grouped_swiglu_mxfp4(const uint16_t* x, const int32_t* offsets
                                        const uint16_t* wd_shared, uint16_t* h, float* y,
                                        PlanEntry* plan, int T, int d, int I, int E, int G,
                                        int R, hipStream_t stream) {
+  if (T <= kDecodeMaxTokens)
+    return launch_skinny<true>(x, offsets, row_token, wg_shared, wu_shared, wd_shared, q, h, y,
+                               plan, T, d, I, E, G, R, stream);
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)

@@ -66,13 +66,19 @@ hipError_t launch_combine(const float* y_rows, const int32_t* slot_row, const fl
                           const float* residual, float* out, int T, int d, int A, int R,
                           hipStream_t stream);
 
-// Upper bound of the grouped GEMM's m-tiles for R rows in G groups.
-inline int64_t max_mtiles(int64_t R, int64_t G) { return R / kGemmBM + G; }
+// Upper bound of the grouped GEMM's m-tiles for R rows in G groups (the smallest m-tile
+// has 32 rows).
+constexpr int kMinTileRows = 32;
+inline int64_t max_mtiles(int64_t R, int64_t G) { return R / kMinTileRows + G; }
 
 // Row pitch (elements) of the intermediate h [R, I]: 64 elements of padding per row, so
 // that the rows one K step of a tile reads do not all share their low address bits.
 constexpr int kHPad = 64;
 inline int64_t h_pitch(int64_t I) { return I + kHPad; }
+
+// bf16 layers with at most 32 tokens (every group fits one 32-row m-tile) run the
+// decode-shaped tiling.
+constexpr int kDecodeMaxTokens = 32;
 
 // bf16 layers whose groups average at least 128 rows run the 256-row tiling.
 inline bool use_wide_tiles(int dtype, int64_t R, int64_t G) {

@@ -63,6 +63,12 @@ SMALL = {c.name: c for c in [
           seed=22).with_(S=2),
     small("soft_bf16_shared_wide", "softmax", "bf16", T=700, d=256, E=4, S=0, I=256, k=2,
           seed=23).with_(S=1),
+    # Decode-shaped bf16 batches (at most 32 tokens: 32-row tiles, K split over 4 waves):
+    # uneven chunks per wave (I = 384), one chunk per wave (d = 256) and waves with none
+    # (I = 128 down), a ragged token count.
+    small("dec_sig_bf16", "sigmoid", "bf16", T=32, d=512, E=40, S=2, I=384, k=6, seed=32),
+    small("dec_soft_bf16_ragged", "softmax", "bf16", T=7, d=256, E=16, S=0, I=128, k=4,
+          seed=33).with_(S=1),
 ]}
 
 # Pre-norm shapes: x is the raw hidden state; the layer runs on RMSNorm(x).
@@ -80,10 +86,24 @@ PRENORM = {c.name: c for c in [
 # Widest supported RMSNorm row (RMSNorm stage only).
 NORM_WIDE = small("norm_wide", "sigmoid", "bf16", T=64, d=16384, E=8, S=0, I=128, k=2,
                   seed=28).with_(prenorm=True, norm_zero_centred=True)
-# MXFP4 routed experts (bf16 shared experts), 128-row tiles.
+# MXFP4 routed experts (bf16 shared experts): decode-shaped tiles up to 32 tokens,
+# 128-row tiles above.
 MXFP4 = {c.name: c for c in [
     small("mx_sig_decode", "sigmoid", "bf16", T=32, d=512, E=40, S=2, I=256, k=6,
           seed=29).with_(weight_format="mxfp4"),
+    # I not a multiple of 256: decode batch on the 128-row tiles
+    small("mx_dec_odd", "sigmoid", "bf16", T=5, d=256, E=16, S=1, I=384, k=4,
+          seed=34).with_(weight_format="mxfp4"),
+    # decode tiles (256-element K spans, 4 waves): three spans of gate/up (d = 768), one
+    # of down; softmax router with an ungated shared expert
+    small("mx_dec_soft", "softmax", "bf16", T=32, d=768, E=24, S=0, I=256, k=8,
+          seed=35).with_(S=1, weight_format="mxfp4"),
+    # one span per GEMM (three waves without work), three tokens
+    small("mx_dec_min", "sigmoid", "bf16", T=3, d=256, E=8, S=1, I=256, k=2,
+          seed=36).with_(weight_format="mxfp4"),
+    # several spans per wave: 8 (gate/up) and 5 (down) spans over 4 waves
+    small("mx_dec_multi", "sigmoid", "bf16", T=24, d=2048, E=16, S=1, I=1280, k=4,
+          seed=37).with_(weight_format="mxfp4"),
     small("mx_sig_rows", "sigmoid", "bf16", T=400, d=256, E=6, S=1, I=256, k=2,
           seed=30).with_(weight_format="mxfp4"),
     small("mx_soft", "softmax", "bf16", T=100, d=512, E=12, S=0, I=128, k=3,
