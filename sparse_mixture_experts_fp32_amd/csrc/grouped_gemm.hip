@@ -448,17 +448,19 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
 // Every group then has at most 32 rows, so one 32-row m-tile per group, and the step is
 // bound by streaming the experts' weights.  A tile is 32 rows x 128 B-rows (gate/up: 64
 // gate + 64 up rows of the same h columns; down: 128 output columns); the 4 waves of a
-// workgroup split its K range into interleaved chunks and each wave loads its A rows and
-// B-rows straight from memory into registers in the MFMA operand layout, double-buffered
-// a chunk ahead, so the K loop has no LDS traffic and no barrier.  The K order inside a
-// chunk is permuted (the product sums over K, so any order shared by A and B is exact) so
-// that each load reads 16 contiguous bytes of a row and, for an MXFP4 B-row, one load is
-// one MX block (16 bytes of codes, one scale byte).  MXFP4 codes are converted to bf16 in
-// registers.  Rows past the group's end load a copy of its last row (their outputs are
-// not stored).  The 4 waves' partial 32 x 128 sums are added in LDS in wave order, then
-// the SwiGLU (gate/up) or the f32 row store (down) runs.  Tiles are taken from a
-// counter, last plan m-tile first, so the shared experts' bf16 tiles (about 4x the bytes
-// of an MXFP4 tile) start before the routed ones.
+// workgroup split its K range into interleaved chunks, double-buffered in registers one
+// chunk ahead, and the K loop has no barrier.  Weights are loaded coalesced (8 lanes x 16
+// bytes cover a 128-byte line of one B-row, so the L1 sends whole-line requests and does
+// one tag lookup per 64 bytes) and pass through the wave's own 16 KB of LDS to the MFMA
+// operand layout; A goes straight into registers in the operand layout.  The K order
+// inside a chunk is permuted (the product sums over K, so any order shared by A and B is
+// exact) so that an A load is 16 contiguous bytes and an MXFP4 operand is one MX block
+// (16 bytes of codes, one scale byte).  MXFP4 codes are converted to bf16 in registers.
+// Rows past the group's end load a copy of its last row (their outputs are not stored).
+// The 4 waves' partial 32 x 128 sums are added in LDS in wave order, then the SwiGLU
+// (gate/up) or the f32 row store (down) runs.  Tiles are taken from a counter, last plan
+// m-tile first, so the shared experts' bf16 tiles (about 4x the bytes of an MXFP4 tile)
+// start before the routed ones.
 constexpr int kSkBM = 32;                 // rows per m-tile
 constexpr int kSkWaves = 4;               // waves per workgroup (K split)
 constexpr int kSkBlocks = 4;              // 32-wide B-row blocks per tile (128 B-rows)
@@ -522,9 +524,9 @@ void grouped_gemm_skinny_kernel(
       // MXFP4 B: chunks of 128 K elements (64 code bytes and 4 scale bytes per B-row).
       // Wave w takes the chunk pairs 8 p + 2 w, 8 p + 2 w + 1 (one 128-byte line of codes
       // and 8 scale bytes per B-row); iteration i of a wave is chunk 8 (i / 2) + 2 w + i % 2.
-      // Load j of a chunk gives lane half hh of B-row n the code bytes 32 j + 16 hh .. +16,
-      // i.e. MX block 2 j + hh of the chunk; MFMA step (j, u) covers K elements
-      // 64 j + 32 hh + 8 u .. +8 of the chunk for A and B alike.
+      // In the operand layout, part j of a chunk gives lane half hh of B-row n the code
+      // bytes 32 j + 16 hh .. +16, i.e. MX block 2 j + hh of the chunk; MFMA step (j, u)
+      // covers K elements 64 j + 32 hh + 8 u .. +8 of the chunk for A and B alike.
       const int nch = K / 128;
       const int nw = 2 * ((nch + 2 * kSkWaves - 1) / (2 * kSkWaves));
       const size_t qbase = ((size_t)g * N + n0) * (K / 2);
@@ -536,24 +538,30 @@ void grouped_gemm_skinny_kernel(
       const __amdgpu_buffer_rsrc_t sr0 = buffer_rsrc(s0 + sbase, sbytes);
       const __amdgpu_buffer_rsrc_t sr1 = buffer_rsrc((MODE == 0 ? s1 : s0) + sbase, sbytes);
       const uint32_t a_voff = a_row + 64 * lh;
-      // Per-block vector offsets (the block's row offset as a scalar offset was slower).
-      uint32_t q_voff[kSkBlocks];
+      // Codes of a chunk pair (128 bytes per B-row) are loaded whole: load q brings tile
+      // rows 8 q + lane / 8 (gate/up: rows 0..63 of q0 for q < 8, of q1 for q >= 8), 16
+      // bytes (lane % 8), and goes through this wave's 16 KB of LDS (its partial-sum
+      // area) to the MFMA layout, the 16-byte slot swizzled by (row / 2) % 8.
+      const uint32_t cq_voff = static_cast<uint32_t>(lane >> 3) * (K / 2) + 16 * (lane & 7);
+      char* stg = reinterpret_cast<char*>(red) + wv * (kSkBlocks * 16 * 64 * 4);
+      uint32_t w_off[2];
 #pragma unroll
-      for (int b = 0; b < kSkBlocks; ++b)
-        q_voff[b] = static_cast<uint32_t>(ln + MOE_SK_BRO(b)) * (K / 2) + 16 * lh;
+      for (int e = 0; e < 2; ++e)
+        w_off[e] = 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((4 * e + (lane >> 4)) & 7));
       const uint32_t s_voff = static_cast<uint32_t>(ln) * (K / 32);
-      u32x4 ra[2][8], rq[2][kSkBlocks][2];
+      u32x4 ra[2][8], rq[16];
       u32x2 rsp[kSkBlocks];          // scale bytes of the current pair
       uint32_t rs_hi[kSkBlocks];     // the pair's second chunk, kept past the next fetch
 #define MOE_SKQ_CHUNK(i) (8 * ((i) >> 1) + 2 * wv + ((i) & 1))
 #define MOE_SKQ_FETCH(i, P)                                                             \
   do {                                                                                  \
     const uint32_t c_ = static_cast<uint32_t>(min(MOE_SKQ_CHUNK(i), nch - 1));          \
+    if ((P) == 0) {                                                                     \
+      _Pragma("unroll") for (int q = 0; q < 16; ++q)                                    \
+          rq[q] = load16((MODE == 0 && q >= 8) ? qr1 : qr0, cq_voff,                    \
+                         8 * (MODE == 0 ? (q & 7) : q) * (K / 2) + c_ * 64);            \
+    }                                                                                   \
     _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                             \
-      const __amdgpu_buffer_rsrc_t qr_ = (MODE == 0 && b >= 2) ? qr1 : qr0;             \
-      const uint32_t qo_ = c_ * 64;                                                     \
-      rq[P][b][0] = load16(qr_, q_voff[b], qo_);                                        \
-      rq[P][b][1] = load16(qr_, q_voff[b], qo_ + 32);                                   \
       if ((P) == 0)                                                                     \
         rsp[b] = __builtin_amdgcn_raw_buffer_load_b64((MODE == 0 && b >= 2) ? sr1 : sr0, \
                                                       s_voff,                           \
@@ -574,7 +582,15 @@ void grouped_gemm_skinny_kernel(
           sw_[b] = rs_hi[b];                                                            \
         }                                                                               \
       }                                                                                 \
+      if ((P) == 0) {                                                                   \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q)                                  \
+            *reinterpret_cast<u32x4*>(stg + 1024 * q + w_off[q & 1]) = rq[q];           \
+      }                                                                                 \
       _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                   \
+        u32x4 cq_[kSkBlocks];                                                           \
+        _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                           \
+            cq_[b] = *reinterpret_cast<const u32x4*>(                                   \
+                stg + 4096 * b + 128 * ln + 16 * ((4 * (P) + 2 * j + lh) ^ ((ln >> 1) & 7))); \
         float sc_[kSkBlocks];                                                           \
         _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                           \
             sc_[b] = mx_scale(sw_[b] >> (8 * (2 * j + lh)));                            \
@@ -582,7 +598,7 @@ void grouped_gemm_skinny_kernel(
           const bf16x8 fa_ = __builtin_bit_cast(bf16x8, ra[P][4 * j + u]);              \
           _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                       \
             const bf16x8 fb_ =                                                          \
-                __builtin_bit_cast(bf16x8, mxfp4_chunk(rq[P][b][j][u], sc_[b]));        \
+                __builtin_bit_cast(bf16x8, mxfp4_chunk(cq_[b][u], sc_[b]));             \
             acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_, fb_, acc[b], 0, 0, 0);\
           }                                                                             \
         }                                                                               \
@@ -606,7 +622,7 @@ void grouped_gemm_skinny_kernel(
     } else {
       // bf16 B: chunks of 64 K elements (128 bytes per B-row), wave w: chunks w, w + 4,
       // ...  MFMA step u, operand half hh covers K elements 32 hh + 8 u .. +8 of the
-      // chunk, so each load reads 16 bytes of both 64-byte halves of the rows' lines.
+      // chunk (16-byte slot 4 hh + u of the row) for A and B alike.
       const int gb = FP4 ? g - E : g;
       const int nch = K / 64;
       const int nw = max(2, ((nch + kSkWaves - 1) / kSkWaves + 1) & ~1);
@@ -615,30 +631,37 @@ void grouped_gemm_skinny_kernel(
       const __amdgpu_buffer_rsrc_t br0 = buffer_rsrc(b0 + bbase, bbytes);
       const __amdgpu_buffer_rsrc_t br1 = buffer_rsrc((MODE == 0 ? b1 : b0) + bbase, bbytes);
       const uint32_t a_voff = a_row + 64 * lh;
-      uint32_t b_voff[kSkBlocks];
+      // Coalesced loads: load q brings tile rows 8 q + lane / 8 (gate/up: rows 0..63 of b0
+      // for q < 8, of b1 for q >= 8), 16 bytes (lane % 8) of the chunk's 128; the chunk
+      // goes through this wave's 16 KB of LDS to the MFMA layout (slot ^ (row / 2) % 8).
+      const uint32_t cb_voff = static_cast<uint32_t>(lane >> 3) * K * 2 + 16 * (lane & 7);
+      char* stg = reinterpret_cast<char*>(red) + wv * (kSkBlocks * 16 * 64 * 4);
+      uint32_t w_off[2];
 #pragma unroll
-      for (int b = 0; b < kSkBlocks; ++b)
-        b_voff[b] = static_cast<uint32_t>(ln + MOE_SK_BRO(b)) * K * 2 + 64 * lh;
-      u32x4 ra[2][4], rb[2][kSkBlocks][4];
+      for (int e = 0; e < 2; ++e)
+        w_off[e] = 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((4 * e + (lane >> 4)) & 7));
+      u32x4 ra[2][4], rb[2][16];
 #define MOE_SKB_FETCH(i, P)                                                             \
   do {                                                                                  \
     const uint32_t c_ = static_cast<uint32_t>(min(wv + kSkWaves * (i), nch - 1));       \
-    _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                             \
-      const __amdgpu_buffer_rsrc_t br_ = (MODE == 0 && b >= 2) ? br1 : br0;             \
-      _Pragma("unroll") for (int u = 0; u < 4; ++u)                                     \
-          rb[P][b][u] = load16(br_, b_voff[b], c_ * 128 + 16 * u);                      \
-    }                                                                                   \
+    _Pragma("unroll") for (int q = 0; q < 16; ++q)                                      \
+        rb[P][q] = load16((MODE == 0 && q >= 8) ? br1 : br0, cb_voff,                   \
+                          8 * (MODE == 0 ? (q & 7) : q) * K * 2 + c_ * 128);            \
     _Pragma("unroll") for (int u = 0; u < 4; ++u)                                       \
         ra[P][u] = load16(a_rsrc, a_voff, c_ * 128 + 16 * u);                           \
   } while (0)
 #define MOE_SKB_MMA(i, P)                                                               \
   do {                                                                                  \
     if (wv + kSkWaves * (i) < nch) {                                                    \
+      _Pragma("unroll") for (int q = 0; q < 16; ++q)                                    \
+          *reinterpret_cast<u32x4*>(stg + 1024 * q + w_off[q & 1]) = rb[P][q];          \
       _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                   \
         const bf16x8 fa_ = __builtin_bit_cast(bf16x8, ra[P][u]);                        \
         _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                           \
             acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                           \
-                fa_, __builtin_bit_cast(bf16x8, rb[P][b][u]), acc[b], 0, 0, 0);         \
+                fa_, *reinterpret_cast<const bf16x8*>(                                  \
+                         stg + 4096 * b + 128 * ln + 16 * ((4 * lh + u) ^ ((ln >> 1) & 7))), \
+                acc[b], 0, 0, 0);                                                       \
       }                                                                                 \
     }                                                                                   \
   } while (0)
