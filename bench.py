@@ -138,6 +138,8 @@ def run(c, steps, warmup, torch):
     res = {
         "T": T, "ms_per_step": ms, "tokens_per_s": T * steps / wall,
         "event_ms_per_step_median": float(np.median(step_ms)),
+        "event_ms_per_step_p10": float(np.percentile(step_ms, 10)),
+        "event_ms_per_step_p90": float(np.percentile(step_ms, 90)),
         "stage_ms": {"route": float(stage[:, 0].mean()), "permute": float(stage[:, 1].mean()),
                      "grouped_swiglu": grouped_ms, "combine": float(stage[:, 3].mean())},
         "layer_tflops": (f_router + f_experts) / (ms * 1e-3) / 1e12,
@@ -223,6 +225,8 @@ def main():
         "roofline": roof,
         "layer_tflops": r["layer_tflops"],
         "layer_frac_bf16_mfma": r["layer_tflops"] / PEAK_BF16_TFLOPS,
+        "step_ms_p10_p50_p90": [r["event_ms_per_step_p10"], r["event_ms_per_step_median"],
+                                r["event_ms_per_step_p90"]],
         "stage_ms": r["stage_ms"],
         "touched_routed_experts": r["touched_routed_experts"],
     }
@@ -230,7 +234,10 @@ def main():
         d = results["inkling_decode"]
         line["decode"] = {
             "workload": "inkling_decode", "T": d["T"], "tokens_per_s": d["tokens_per_s"],
-            "ms_per_step": d["ms_per_step"], "stage_ms": d["stage_ms"],
+            "ms_per_step": d["ms_per_step"],
+            "step_ms_p10_p50_p90": [d["event_ms_per_step_p10"], d["event_ms_per_step_median"],
+                                    d["event_ms_per_step_p90"]],
+            "stage_ms": d["stage_ms"],
             "touched_routed_experts": d["touched_routed_experts"],
             "roofline": {"bound": "hbm", "achieved": d["grouped_gbs"], "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": d["grouped_gbs"] / PEAK_HBM_GBS,

@@ -102,10 +102,17 @@ CONFIGS: dict[str, MoEConfig] = {
                                 k=16, router="sigmoid", dtype="bf16", x_std=1.0,
                                 w_std=0.02, bias_std=0.1, zipf_s=0.0, zipf_hot_share=0.0,
                                 seed=6, prenorm=True),
+    # One GPU's share of the Inkling prefill layer under 8-way expert parallelism: the 32
+    # routed experts it would own receive ~49,152 rows (8,192 tokens x 6 per GPU, spread
+    # over 8 owners), plus the replicated shared experts on its own 8,192 tokens.  Routing
+    # 8,192 local tokens over the 32 local experts gives the grouped GEMMs that shape.
+    "inkling_ep8_share": MoEConfig(name="inkling_ep8_share", T=8192, seed=8,
+                                   **{**_INKLING, "E": 32}),
 }
 
 # The order in which the five workloads are listed everywhere.
 CONFIG_ORDER = ["tiny_fp32", "inkling_decode", "inkling_prefill", "qwen38", "inkling_skewed"]
 # Workloads beyond the five above: Qwen3.8 with its ungated shared expert; Kimi K3-style
-# latent experts behind a pre-norm RMSNorm; the Inkling decode batch with MXFP4 weights.
-EXTRA_ORDER = ["qwen38_shared", "kimi_k3_latent", "inkling_decode_mxfp4"]
+# latent experts behind a pre-norm RMSNorm; the Inkling decode batch with MXFP4 weights;
+# one GPU's expert-parallel share of the Inkling prefill layer.
+EXTRA_ORDER = ["qwen38_shared", "kimi_k3_latent", "inkling_decode_mxfp4", "inkling_ep8_share"]

@@ -335,7 +335,7 @@ def test_zero_router_tie_rule_on_gpu():
 # ------------------------------------------------------------------------ full size
 FULL_SAMPLE = {"inkling_decode": None, "inkling_prefill": 48, "qwen38": 24,
                "inkling_skewed": 48, "qwen38_shared": 24, "kimi_k3_latent": 48,
-               "inkling_decode_mxfp4": None}
+               "inkling_decode_mxfp4": None, "inkling_ep8_share": 48}
 
 
 @pytest.mark.parametrize("name", list(FULL_SAMPLE))
