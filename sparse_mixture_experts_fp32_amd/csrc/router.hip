@@ -154,14 +154,36 @@ __global__ __launch_bounds__(256) void topk_kernel(
   const bool live = t < T;
   float raw[MAXV];
   uint64_t key[MAXV];
+  // Logits: the nsplit partial sums added in split order.  The loads of 8 splits of every
+  // slot are issued together (a runtime-length loop of dependent adds per slot would
+  // serialize nsplit x MAXV memory latencies); the adds keep the order, and the padding
+  // +0 terms cannot change a sum that starts at +0.
+  float lsum[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) lsum[i] = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float pv[8][MAXV];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i) {
+        const int e = lane + 64 * i;
+        pv[u][i] = (live && e < NE && s0 + u < nsplit)
+                       ? part[((size_t)(s0 + u) * T + t) * NE + e]
+                       : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i) lsum[i] += pv[u][i];
+  }
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int e = lane + 64 * i;
     raw[i] = 0.f;
     key[i] = 0;
     if (live && e < NE) {
-      float l = 0.f;
-      for (int s = 0; s < nsplit; ++s) l += part[((size_t)s * T + t) * NE + e];
+      float l = lsum[i];
       if (logit_offset != nullptr && e < E) l += logit_offset[e];
       float sel;
       if (router == 1) {
