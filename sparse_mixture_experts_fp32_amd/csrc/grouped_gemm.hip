@@ -30,7 +30,6 @@
 
 namespace moe {
 
-constexpr int kRowBytes = 128;
 constexpr int kBM = kGemmBM;                  // 128
 constexpr int kBRows = 256;
 constexpr int kStageA = kBM * kRowBytes;      // 16 KB
@@ -38,27 +37,6 @@ constexpr int kStageB = kBRows * kRowBytes;   // 32 KB
 constexpr int kStage = kStageA + kStageB;     // 48 KB
 constexpr int kStages = 2;                    // 96 KB of the CU's 160 KB
 constexpr int kNB = 4;                        // n-tiles per scheduling block
-
-// gfx950's LDS serves a ds_read_b128 16 lanes (256 bytes, 64 banks) at a time; the
-// fragment reads of one phase touch 16 consecutive rows at one chunk.  Rows 2j and 2j+1
-// fall in different bank halves, and the XOR with (row / 2) % 8 spreads the 8 row pairs
-// over the 8 chunk slots, so one phase hits 16 distinct bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
-}
-
-// Raw buffer resource over [base, base + bytes): loads past the end return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base,
-                                                              uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
-                                           0x00020000);
-}
-
-// 16 bytes per lane from buffer offset voffset + soffset (buffer_load_dwordx4).
-__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
-                                        uint32_t soffset) {
-  return __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, soffset, 0);
-}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 

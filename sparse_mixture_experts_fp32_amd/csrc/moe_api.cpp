@@ -28,6 +28,7 @@ struct Layout {
 struct Dims {
   int64_t T, d, E, S, I, k, A, G, R;
   int64_t NR;  // router rows: E + S (sigmoid) or E (softmax: ungated shared experts)
+  int dtype;
 };
 
 Dims dims_of(const moe_config_t& c, int64_t T) {
@@ -40,6 +41,7 @@ Dims dims_of(const moe_config_t& c, int64_t T) {
   m.k = c.top_k;
   m.A = m.k + m.S;
   m.G = m.E + m.S;
+  m.dtype = c.dtype;
   m.R = T * m.A;
   m.NR = c.router == MOE_ROUTER_SIGMOID_SHARED ? m.G : m.E;
   return m;
@@ -47,8 +49,8 @@ Dims dims_of(const moe_config_t& c, int64_t T) {
 
 // Router K split: enough workgroups to cover the chip at small T, chunks of >= 256.
 void router_split(const Dims& m, int* nsplit, int* kchunk) {
-  const int64_t tiles = ((m.T + moe::kRouterTile - 1) / moe::kRouterTile) *
-                        ((m.NR + moe::kRouterTile - 1) / moe::kRouterTile);
+  const int64_t tile = moe::router_tile(m.dtype, m.T);
+  const int64_t tiles = ((m.T + tile - 1) / tile) * ((m.NR + tile - 1) / tile);
   int64_t maxsplit = m.d / 256 > 0 ? m.d / 256 : 1;
   int64_t want = tiles > 0 ? (512 + tiles - 1) / tiles : 1;
   int64_t ns = want < maxsplit ? want : maxsplit;

@@ -1,5 +1,6 @@
 // Device-side helpers shared by the gfx950 kernels of the MoE layer: storage types,
-// bf16 conversion, MFMA operand types and wave-wide reductions.
+// bf16 conversion, MFMA operand types, wave-wide reductions, buffer loads and the LDS
+// row swizzle.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -47,6 +48,30 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     v = o > v ? o : v;
   }
   return v;
+}
+
+// LDS tiles are rows of one 128-byte K step (64 bf16 or 32 f32 elements).
+constexpr int kRowBytes = 128;
+
+// gfx950's LDS serves a ds_read_b128 16 lanes (256 bytes, 64 banks) at a time; the
+// fragment reads of one phase touch 16 consecutive rows at one chunk.  Rows 2j and 2j+1
+// fall in different bank halves, and the XOR with (row / 2) % 8 spreads the 8 row pairs
+// over the 8 chunk slots, so one phase hits 16 distinct bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base,
+                                                              uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
+                                           0x00020000);
+}
+
+// 16 bytes per lane from buffer offset voffset + soffset (buffer_load_dwordx4).
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
+                                        uint32_t soffset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, soffset, 0);
 }
 
 // Workgroup id remap so that the workgroups the dispatcher places on one XCD

@@ -13,7 +13,14 @@ constexpr int kGemmBM = 128;        // grouped rows per tile
 constexpr int kGateUpBN = 128;      // h columns per gate/up tile (128 gate + 128 up rows)
 constexpr int kDownBN = 256;        // y columns per down tile
 constexpr int kPermBlock = 256;     // tokens per permute block
-constexpr int kRouterTile = 64;     // tokens and experts per router tile
+constexpr int kRouterTile = 64;     // tokens and experts per router tile (small batches)
+constexpr int kRouterBigTile = 128; // tokens and experts per router tile, bf16, T >= 256
+
+// Router tile edge for a batch: bf16 batches of at least 256 tokens use the LDS-staged
+// 128 x 128 tiles.
+inline int router_tile(int dtype, int64_t T) {
+  return (dtype == 1 && T >= 2 * kRouterBigTile) ? kRouterBigTile : kRouterTile;
+}
 
 struct PlanEntry {   // one m-tile of the grouped GEMM
   int32_t group, row0, nrows, pad;
