@@ -7,7 +7,8 @@ over one batch of seeded synthetic inputs already resident in HBM.  The headline
 workload is the Inkling-shaped prefill batch (T = 8,192), where the layer is bound by
 bf16 MFMA throughput; the Inkling-shaped decode batch (T = 32), bound by streaming the
 active experts' weights from HBM, is measured in the same run and reported in the same
-JSON line under "decode".  Rank 0 prints one JSON line.
+JSON line under "decode", and the same decode batch with MXFP4 routed-expert weights
+under "decode_mxfp4".  Rank 0 prints one JSON line.
 
 Per-stage durations come from HIP events recorded on the launch stream between the
 C-ABI calls of every timed step.  The dominant kernel work is the grouped SwiGLU step
@@ -74,7 +75,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", nargs="*", default=["inkling_prefill", "inkling_decode"])
+    p.add_argument("--workload", nargs="*",
+                   default=["inkling_prefill", "inkling_decode", "inkling_decode_mxfp4"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=512,
                    help="tokens of the prefill batch the oracle is timed on")
@@ -230,10 +232,12 @@ def main():
         "stage_ms": r["stage_ms"],
         "touched_routed_experts": r["touched_routed_experts"],
     }
-    if "inkling_decode" in results and head != "inkling_decode":
-        d = results["inkling_decode"]
-        line["decode"] = {
-            "workload": "inkling_decode", "T": d["T"], "tokens_per_s": d["tokens_per_s"],
+    for key, name in (("decode", "inkling_decode"), ("decode_mxfp4", "inkling_decode_mxfp4")):
+        if name not in results or head == name:
+            continue
+        d = results[name]
+        line[key] = {
+            "workload": name, "T": d["T"], "tokens_per_s": d["tokens_per_s"],
             "ms_per_step": d["ms_per_step"],
             "step_ms_p10_p50_p90": [d["event_ms_per_step_p10"], d["event_ms_per_step_median"],
                                     d["event_ms_per_step_p90"]],
@@ -241,7 +245,7 @@ def main():
             "touched_routed_experts": d["touched_routed_experts"],
             "roofline": {"bound": "hbm", "achieved": d["grouped_gbs"], "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": d["grouped_gbs"] / PEAK_HBM_GBS,
-                         "traffic": profiled_traffic("inkling_decode")},
+                         "traffic": profiled_traffic(name)},
             "layer_alg_gbs": d["layer_alg_gbs"],
             "layer_frac_hbm": d["layer_alg_gbs"] / PEAK_HBM_GBS,
         }
