@@ -10,12 +10,22 @@
 //             round h to bf16 once (nearest even).
 //   down:     y[r, n] = sum_i h[r, i] Wd[n, i], f32 accumulation and f32 output.
 //
-// Work decomposition.  A device-built plan lists the m-tiles (up to 128 rows of one
-// group).  Tiles are ordered group by group; inside a group in blocks of 4 n-tiles, m-tile
-// by m-tile, so the workgroups that run together on one XCD share a few weight slices
-// (read from HBM once, then from L2) and a few sets of gathered rows.
-// The grid is persistent (one workgroup per CU); each XCD walks one contiguous range of
-// tiles.
+// Three tilings share the grouped-row layout and the m-tile plan (below):
+//   - 128 rows x 256 B-rows (grouped_gemm_kernel): f32 layers and bf16 layers whose
+//     groups average fewer than 128 rows, with more than 32 tokens;
+//   - 256 x 256 (grouped_gemm_wide_kernel): bf16 layers whose groups average 128 rows or
+//     more;
+//   - 32 x 128 with K split over four waves (grouped_gemm_skinny_kernel): bf16 layers of
+//     at most 32 tokens, where the step streams weights.
+// Routed experts may hold MXFP4 weights (4-bit codes, one power-of-two scale per 32
+// elements along K); the 128-row and 32-row tilings expand them to bf16 on the way to
+// the MFMAs.
+//
+// Work decomposition (128-row tiling).  A device-built plan lists the m-tiles (up to 128
+// rows of one group).  Tiles are ordered group by group; inside a group in blocks of 4
+// n-tiles, m-tile by m-tile, so the workgroups that run together on one XCD share a few
+// weight slices (read from HBM once, then from L2) and a few sets of gathered rows.  The
+// grid is persistent (one workgroup per CU); each XCD walks one contiguous range of tiles.
 //
 // Tile: 128 rows x 256 B-rows (gate/up: 128 gate + 128 up rows; down: 256 outputs).  K
 // moves 128 bytes per row per step (64 bf16 / 32 f32).  Each step is fetched from global
@@ -23,8 +33,9 @@
 // LDS buffers with ds_write_b128; on gfx950 this outruns direct buffer->LDS loads, whose
 // LDS writes throttled the whole pipeline.  LDS rows are 128 B; 16-byte chunk c of row r
 // sits at slot c ^ ((r / 2) % 8).  A wave writes each 1 KB block as 64 lanes x 16 B, so
-// each lane fetches the global chunk that belongs at its slot.  Eight waves (two per SIMD, so one wave's MFMAs cover the
-// other's waits) in 2 x 4; each owns 64 rows x 64 B-rows as 2 x 2 MFMA 32x32 tiles.
+// each lane fetches the global chunk that belongs at its slot.  Eight waves (two per
+// SIMD, so one wave's MFMAs cover the other's waits) in 2 x 4; each owns 64 rows x 64
+// B-rows as 2 x 2 MFMA 32x32 tiles.
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -50,7 +61,9 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t
 
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt in bits 3:0
 // and 15:14, expcnt 6:4, lgkmcnt 11:8).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int vmcnt_imm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
 
 // MXFP4 (OCP Microscaling FP4) decode with gfx950's scaled conversion: one
 // v_cvt_scalef32_pk_bf16_fp4 turns the two E2M1 codes of one byte (element 0 in the low
@@ -60,7 +73,9 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // the E8M0 format defines.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float mx_scale(uint32_t s) { return __uint_as_float((s & 0xffu) << 23); }
+__device__ __forceinline__ float mx_scale(uint32_t s) {
+  return __uint_as_float((s & 0xffu) << 23);
+}
 // 8 codes (one 32-bit word, element i in bits 4i..4i+3) -> 8 bf16 (one 16-byte chunk,
 // element i in halfword i).
 __device__ __forceinline__ u32x4 mxfp4_chunk(uint32_t w, float sc) {
@@ -446,7 +461,7 @@ constexpr int kSkBlocks = 4;              // 32-wide B-row blocks per tile (128 
 template <int MODE, bool FP4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void grouped_gemm_skinny_kernel(
-    const uint16_t* __restrict__ a_src,      // MODE 0: x [T, K]; MODE 1: h [R, K] (pitch lda)
+    const uint16_t* __restrict__ a_src,      // MODE 0: x [T, K]; MODE 1: h [R, K]
     const int32_t* __restrict__ row_token,   // MODE 0 only
     const uint16_t* __restrict__ b0,         // bf16 B: MODE 0 gate, MODE 1 down [., N, K]
     const uint16_t* __restrict__ b1,         // bf16 B: MODE 0 up
@@ -501,7 +516,8 @@ void grouped_gemm_skinny_kernel(
     if (quant) {
       // MXFP4 B: chunks of 128 K elements (64 code bytes and 4 scale bytes per B-row).
       // Wave w takes the chunk pairs 8 p + 2 w, 8 p + 2 w + 1 (one 128-byte line of codes
-      // and 8 scale bytes per B-row); iteration i of a wave is chunk 8 (i / 2) + 2 w + i % 2.
+      // and 8 scale bytes per B-row); iteration i of a wave is chunk
+      // 8 (i / 2) + 2 w + i % 2.
       // In the operand layout, part j of a chunk gives lane half hh of B-row n the code
       // bytes 32 j + 16 hh .. +16, i.e. MX block 2 j + hh of the chunk; MFMA step (j, u)
       // covers K elements 64 j + 32 hh + 8 u .. +8 of the chunk for A and B alike.
@@ -541,9 +557,9 @@ void grouped_gemm_skinny_kernel(
     }                                                                                   \
     _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                             \
       if ((P) == 0)                                                                     \
-        rsp[b] = __builtin_amdgcn_raw_buffer_load_b64((MODE == 0 && b >= 2) ? sr1 : sr0, \
-                                                      s_voff,                           \
-                                                      MOE_SK_BRO(b) * (K / 32) + c_ * 4, 0); \
+        rsp[b] = __builtin_amdgcn_raw_buffer_load_b64(                                  \
+            (MODE == 0 && b >= 2) ? sr1 : sr0, s_voff, MOE_SK_BRO(b) * (K / 32) + c_ * 4,   \
+            0);                                                                         \
     }                                                                                   \
     _Pragma("unroll") for (int u = 0; u < 8; ++u)                                       \
         ra[P][u] = load16(a_rsrc, a_voff, c_ * 256 + 128 * (u >> 2) + 16 * (u & 3));    \
@@ -568,7 +584,8 @@ void grouped_gemm_skinny_kernel(
         u32x4 cq_[kSkBlocks];                                                           \
         _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                           \
             cq_[b] = *reinterpret_cast<const u32x4*>(                                   \
-                stg + 4096 * b + 128 * ln + 16 * ((4 * (P) + 2 * j + lh) ^ ((ln >> 1) & 7))); \
+                stg + 4096 * b + 128 * ln +                                             \
+                16 * ((4 * (P) + 2 * j + lh) ^ ((ln >> 1) & 7)));                       \
         float sc_[kSkBlocks];                                                           \
         _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                           \
             sc_[b] = mx_scale(sw_[b] >> (8 * (2 * j + lh)));                            \
@@ -637,8 +654,9 @@ void grouped_gemm_skinny_kernel(
         const bf16x8 fa_ = __builtin_bit_cast(bf16x8, ra[P][u]);                        \
         _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                           \
             acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                           \
-                fa_, *reinterpret_cast<const bf16x8*>(                                  \
-                         stg + 4096 * b + 128 * ln + 16 * ((4 * lh + u) ^ ((ln >> 1) & 7))), \
+                fa_,                                                                    \
+                *reinterpret_cast<const bf16x8*>(                                       \
+                    stg + 4096 * b + 128 * ln + 16 * ((4 * lh + u) ^ ((ln >> 1) & 7))), \
                 acc[b], 0, 0, 0);                                                       \
       }                                                                                 \
     }                                                                                   \
@@ -691,7 +709,8 @@ void grouped_gemm_skinny_kernel(
       for (int r = 0; r < 16; ++r) {
         float ys = 0.0f;
 #pragma unroll
-        for (int w2 = 0; w2 < kSkWaves; ++w2) ys += red[((w2 * kSkBlocks + wv) * 16 + r) * 64 + lane];
+        for (int w2 = 0; w2 < kSkWaves; ++w2)
+          ys += red[((w2 * kSkBlocks + wv) * 16 + r) * 64 + lane];
         const int m = 8 * (r >> 2) + 4 * lh + (r & 3);
         if (m < nrows) y[(size_t)(row0 + m) * ldc + n0 + 32 * wv + ln] = ys;
       }

@@ -91,17 +91,18 @@ NORM_WIDE = small("norm_wide", "sigmoid", "bf16", T=64, d=16384, E=8, S=0, I=128
 MXFP4 = {c.name: c for c in [
     small("mx_sig_decode", "sigmoid", "bf16", T=32, d=512, E=40, S=2, I=256, k=6,
           seed=29).with_(weight_format="mxfp4"),
-    # I not a multiple of 256: decode batch on the 128-row tiles
+    # decode tiles with one chunk pair for four waves (d = 256) and an odd number of down
+    # chunks (I = 384: three, the last pair half empty)
     small("mx_dec_odd", "sigmoid", "bf16", T=5, d=256, E=16, S=1, I=384, k=4,
           seed=34).with_(weight_format="mxfp4"),
-    # decode tiles (256-element K spans, 4 waves): three spans of gate/up (d = 768), one
-    # of down; softmax router with an ungated shared expert
+    # decode tiles: six gate/up chunks over four waves (d = 768), two down chunks; softmax
+    # router with an ungated shared expert
     small("mx_dec_soft", "softmax", "bf16", T=32, d=768, E=24, S=0, I=256, k=8,
           seed=35).with_(S=1, weight_format="mxfp4"),
-    # one span per GEMM (three waves without work), three tokens
+    # two chunks per GEMM (three waves without work), three tokens
     small("mx_dec_min", "sigmoid", "bf16", T=3, d=256, E=8, S=1, I=256, k=2,
           seed=36).with_(weight_format="mxfp4"),
-    # several spans per wave: 8 (gate/up) and 5 (down) spans over 4 waves
+    # several chunk pairs per wave: 16 gate/up and 10 down chunks over 4 waves
     small("mx_dec_multi", "sigmoid", "bf16", T=24, d=2048, E=16, S=1, I=1280, k=4,
           seed=37).with_(weight_format="mxfp4"),
     small("mx_sig_rows", "sigmoid", "bf16", T=400, d=256, E=6, S=1, I=256, k=2,
