@@ -53,10 +53,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // 16 bytes per lane from buffer offset voffset + soffset straight into LDS at
 // lds_wave_base + 16 * lane (buffer_load_dwordx4 ... lds; counted by vmcnt).
+template <int POLICY = kCached>
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
                                            uint32_t soffset, char* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds_wave_base), 16, voffset,
-                                           soffset, 0, 0);
+                                           soffset, 0, POLICY);
 }
 
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt in bits 3:0
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
     _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
         ra[P][i] = load16(a_rsrc, a_off[i], k0_);                                       \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                       \
-        rb[P][i] = load16(b_rsrc, b_off[i], k0_);                                       \
+        rb[P][i] = load16<kStream>(b_rsrc, b_off[i], k0_);                              \
   } while (0)
 #define MOE_STORE(kt, P)                                                                \
   do {                                                                                  \
@@ -552,8 +553,8 @@ void grouped_gemm_skinny_kernel(
     const uint32_t c_ = static_cast<uint32_t>(min(MOE_SKQ_CHUNK(i), nch - 1));          \
     if ((P) == 0) {                                                                     \
       _Pragma("unroll") for (int q = 0; q < 16; ++q)                                    \
-          rq[q] = load16((MODE == 0 && q >= 8) ? qr1 : qr0, cq_voff,                    \
-                         8 * (MODE == 0 ? (q & 7) : q) * (K / 2) + c_ * 64);            \
+          rq[q] = load16<kStream>((MODE == 0 && q >= 8) ? qr1 : qr0, cq_voff,           \
+                                  8 * (MODE == 0 ? (q & 7) : q) * (K / 2) + c_ * 64);   \
     }                                                                                   \
     _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                             \
       if ((P) == 0)                                                                     \
@@ -640,8 +641,8 @@ void grouped_gemm_skinny_kernel(
   do {                                                                                  \
     const uint32_t c_ = static_cast<uint32_t>(min(wv + kSkWaves * (i), nch - 1));       \
     _Pragma("unroll") for (int q = 0; q < 16; ++q)                                      \
-        rb[P][q] = load16((MODE == 0 && q >= 8) ? br1 : br0, cb_voff,                   \
-                          8 * (MODE == 0 ? (q & 7) : q) * K * 2 + c_ * 128);            \
+        rb[P][q] = load16<kStream>((MODE == 0 && q >= 8) ? br1 : br0, cb_voff,          \
+                                   8 * (MODE == 0 ? (q & 7) : q) * K * 2 + c_ * 128);   \
     _Pragma("unroll") for (int u = 0; u < 4; ++u)                                       \
         ra[P][u] = load16(a_rsrc, a_voff, c_ * 128 + 16 * u);                           \
   } while (0)
@@ -890,8 +891,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
     if (loader) {                                                                       \
       char* st_ = smem + ((2 * (k)) % kWSlots) * kWHalf + lw * (kWNB * 1024);           \
       _Pragma("unroll") for (int i = (i0); i < (i0) + kWNB / 2; ++i)                    \
-          load_lds16(b_rsrc, b_base[i & 1], (k) * kRowBytes + (i >> 1) * b_pair,        \
-                     st_ + i * 1024);                                                   \
+          load_lds16<MODE == 0 ? kStream : kCached>(                                    \
+              b_rsrc, b_base[i & 1], (k) * kRowBytes + (i >> 1) * b_pair, st_ + i * 1024); \
     }                                                                                   \
   } while (0)
 

@@ -68,10 +68,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base,
                                            0x00020000);
 }
 
+// Cache policy of a load: kStream marks data read once (weights streamed from HBM) as
+// non-temporal, so it does not push the reused rows and scales out of the L1.
+constexpr int kCached = 0;
+constexpr int kStream = 2;
+
 // 16 bytes per lane from buffer offset voffset + soffset (buffer_load_dwordx4).
+template <int POLICY = kCached>
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
                                         uint32_t soffset) {
-  return __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, soffset, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, soffset, POLICY);
 }
 
 // Workgroup id remap so that the workgroups the dispatcher places on one XCD
