@@ -78,7 +78,7 @@ def parse():
     p.add_argument("--workload", nargs="*",
                    default=["inkling_prefill", "inkling_decode", "inkling_decode_mxfp4"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=512,
+    p.add_argument("--cpu-sample", type=int, default=1024,
                    help="tokens of the prefill batch the oracle is timed on")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="first run one plain device-to-device copy of BYTES bytes, the "

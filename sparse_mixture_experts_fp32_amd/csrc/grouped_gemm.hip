@@ -338,7 +338,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
     const uint32_t k0_ = (kt) * kRowBytes;                                              \
     _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
         ra[P][i] = load16(a_rsrc, a_off[i], k0_);                                       \
-    rq[P] = load16(q_rsrc, q_off, (kt) * 32);                                           \
+    rq[P] = load16<kStream>(q_rsrc, q_off, (kt) * 32);                                  \
     rs[P] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_off, (kt) * 2, 0);            \
   } while (0)
 #define MOE_STOREQ(kt, P)                                                               \
