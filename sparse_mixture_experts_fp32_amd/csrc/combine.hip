@@ -19,7 +19,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
   __shared__ int32_t rows[kMaxActive];
   __shared__ float wts[kMaxActive];
   const int t = blockIdx.x;
-  if (threadIdx.x < A) {
+  if (static_cast<int>(threadIdx.x) < A) {
     const int r = slot_row[(size_t)t * A + threadIdx.x];
     rows[threadIdx.x] = min(max(r, 0), R - 1);
     wts[threadIdx.x] = weights[(size_t)t * A + threadIdx.x];

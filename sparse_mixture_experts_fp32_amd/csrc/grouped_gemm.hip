@@ -784,7 +784,6 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
   for (int mi = 0; mi < 4; ++mi) arow[mi] = wm * 128 + mi * 32 + (lane & 31);
   const __amdgpu_buffer_rsrc_t a_rsrc = buffer_rsrc(a_src, a_bytes);
   const int KT = K * static_cast<int>(sizeof(TE)) / kRowBytes;
-  const int H = 2 * KT;
 
   uint32_t phase = 0;
   for (uint32_t logical = lo + blockIdx.x / kXcds; logical < hi;

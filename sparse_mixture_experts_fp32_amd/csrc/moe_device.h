@@ -17,10 +17,6 @@ constexpr int kWave = 64;  // CDNA wavefront width
 constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, 32 CUs each
 
 // bf16 is stored as its raw 16-bit pattern.
-struct bf16_t {
-  uint16_t bits;
-};
-
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
@@ -78,15 +74,6 @@ template <int POLICY = kCached>
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
                                         uint32_t soffset) {
   return __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, soffset, POLICY);
-}
-
-// Workgroup id remap so that the workgroups the dispatcher places on one XCD
-// (consecutive ids go round-robin over the 8 XCDs) receive a contiguous range of
-// logical tile ids, which then share that XCD's L2.  A bijection on [0, n).
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t p, uint32_t n) {
-  uint32_t xcd = p % kXcds, j = p / kXcds;
-  uint32_t q = n / kXcds, r = n % kXcds;
-  return xcd * q + (xcd < r ? xcd : r) + j;
 }
 
 }  // namespace moe

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restric
 // within group e.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ block_hist,
                                                          int nblocks, int T, int E, int S,
-                                                         int k, int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets) {
   __shared__ int32_t scan[1024];
   const int G = E + S;
@@ -115,7 +115,7 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int S, int k,
   hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(kPermBlock), E * sizeof(int32_t),
                      stream, topk_idx, T, E, k, block_hist);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, stream, block_hist, nb, T, E,
-                     S, k, counts, offsets);
+                     S, counts, offsets);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(kPermBlock),
                      4 * E * sizeof(unsigned long long), stream, topk_idx, T, E, S, k,
                      block_hist, row_token, slot_row);
