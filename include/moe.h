@@ -176,6 +176,24 @@ moe_status_t moe_forward_rmsnorm(const moe_config_t* cfg, int64_t T, const void*
                                  float* out, int32_t* topk_idx_out, int32_t* counts_out,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Packed MXFP4 scales.  The MXFP4 entry points below take each weight tensor's E8M0
+ * scales, defined row-major as [E, N, K/32] (row n, MX block kb = elements 32 kb .. +31 of
+ * K), in a packed order: for each expert e, each block of 64 rows nb and each run of 8 MX
+ * blocks kr, a 512-byte record of 64 rows x 8 bytes,
+ *   packed[(((e * N/64 + nb) * KR + kr) * 64 + r) * 8 + j] = scale[e, 64 nb + r, 8 kr + j]
+ * with KR = ceil(K / 256) and zero bytes where 8 kr + j >= K/32.  One wave's scales for 32
+ * rows and 256 elements of K are then 256 contiguous bytes.  Weights are packed once, when
+ * they are loaded.
+ *
+ * moe_mxfp4_scales_bytes (host only): size of the packed tensor, E * (N/64) * KR * 512.
+ * moe_mxfp4_pack_scales: scales (device, [E, N, K/32] uint8) -> packed (device, that
+ * size, 16-byte aligned, not overlapping scales), enqueued on stream.
+ * Both: MOE_ERR_ARG for E, N or K <= 0 or a NULL / misaligned pointer; MOE_ERR_UNSUPPORTED
+ * unless N % 64 == 0 and K % 32 == 0, or if one expert's packed scales reach 2 GiB. */
+moe_status_t moe_mxfp4_scales_bytes(int64_t E, int64_t N, int64_t K, size_t* bytes);
+moe_status_t moe_mxfp4_pack_scales(int64_t E, int64_t N, int64_t K, const uint8_t* scales,
+                                   uint8_t* packed, hipStream_t stream);
+
 /* MXFP4 routed experts (next to the decode shape's HBM bound: ~4.25 bits per weight).
  * The routed experts' weights arrive block-scaled FP4: Inkling's FP4 checkpoint keeps its
  * shared experts in BF16 ("Inkling vs Gemma 4 31B", shared-expert row) and the pages name
@@ -184,10 +202,11 @@ moe_status_t moe_forward_rmsnorm(const moe_config_t* cfg, int64_t T, const void*
  * E8M0 scale byte s (2^(s - 127), 255 = NaN), elements E2M1 (sign, 2 exponent bits with
  * bias 1, 1 mantissa bit), two per byte with element 2i in the low nibble.  The experts
  * compute on the exactly dequantized weights with bf16 x, as in moe_grouped_swiglu.
- *   wq_gate, wq_up [E, I, d/2] uint8, ws_gate, ws_up [E, I, d/32] uint8;
- *   wq_down [E, d, I/2] uint8, ws_down [E, d, I/32] uint8 (codes 16-byte aligned);
+ *   wq_gate, wq_up [E, I, d/2] uint8; ws_gate, ws_up the packed scales of [E, I, d/32]
+ *   (moe_mxfp4_pack_scales with N = I, K = d); wq_down [E, d, I/2] uint8; ws_down the
+ *   packed scales of [E, d, I/32] (N = d, K = I); codes and scales 16-byte aligned;
  *   w_gate_shared, w_up_shared [S, I, d] bf16, w_down_shared [S, d, I] bf16 (NULL iff
- *   S = 0).  bf16 layers only (MOE_ERR_UNSUPPORTED otherwise); 128-row tiles. */
+ *   S = 0).  bf16 layers only (MOE_ERR_UNSUPPORTED otherwise). */
 moe_status_t moe_grouped_swiglu_mxfp4(const moe_config_t* cfg, int64_t T, const void* x,
                                       const int32_t* offsets, const int32_t* row_token,
                                       const uint8_t* wq_gate, const uint8_t* ws_gate,

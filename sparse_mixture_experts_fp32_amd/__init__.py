@@ -5,6 +5,6 @@ from .moe import (  # noqa: F401
     MOE_F32, MOE_OK, MOE_ROUTER_SIGMOID_SHARED, MOE_ROUTER_SOFTMAX_TOPK, MoEError,
     header_functions, load_library, make_config, moe_combine, moe_config_t, moe_forward,
     moe_forward_mxfp4, moe_forward_rmsnorm, moe_grouped_swiglu, moe_grouped_swiglu_mxfp4,
-    moe_permute, moe_rmsnorm, moe_route,
+    moe_mxfp4_pack_scales, moe_mxfp4_scales_bytes, moe_permute, moe_rmsnorm, moe_route,
     moe_workspace_size, status_str,
 )

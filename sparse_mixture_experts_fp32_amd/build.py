@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe.so")
 OBJ = os.path.join(PKG, "_build")
 
-HIP_SOURCES = ["rmsnorm.hip", "router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip"]
+HIP_SOURCES = ["rmsnorm.hip", "router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip",
+               "mx_scales.hip"]
 CXX_SOURCES = ["moe_api.cpp"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

@@ -18,8 +18,8 @@
 //   - 32 x 128 with K split over four waves (grouped_gemm_skinny_kernel): bf16 layers of
 //     at most 32 tokens, where the step streams weights.
 // Routed experts may hold MXFP4 weights (4-bit codes, one power-of-two scale per 32
-// elements along K); the 128-row and 32-row tilings expand them to bf16 on the way to
-// the MFMAs.
+// elements along K, the scales packed in records of 64 rows x 8 MX blocks); the 128-row
+// and 32-row tilings expand them to bf16 on the way to the MFMAs.
 //
 // Work decomposition (128-row tiling).  A device-built plan lists the m-tiles (up to 128
 // rows of one group).  Tiles are ordered group by group; inside a group in blocks of 4
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
     uint32_t a_bytes,                       // bytes of a_src
     int K, int N, int T, int NT,
     int lda, int ldc,                       // row pitch (elements) of a_src and c_out
-    // FP4: the E routed experts' B in MXFP4 (codes [E, N, K/2], scales [E, N, K/32];
+    // FP4: the E routed experts' B in MXFP4 (codes [E, N, K/2], packed scales;
     // MODE 0: q0/s0 gate, q1/s1 up; MODE 1: q0/s0 down); b0/b1 then hold only the shared
     // experts, expert g >= E at index g - E.
     const uint8_t* __restrict__ q0, const uint8_t* __restrict__ q1,
@@ -327,10 +327,15 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
       const int qrows = MODE == 0 ? kGateUpBN : kDownBN;
       const __amdgpu_buffer_rsrc_t q_rsrc = buffer_rsrc(
           qsrc + ((size_t)g * N + n0) * (K / 2), static_cast<uint32_t>(qrows * (K / 2)));
+      // Packed scales (records of 64 rows x 8 MX blocks): MX block 2 kt + qhalf of tile
+      // row qlocal is byte 2 (kt % 4) + qhalf of its row in record kt / 4.
+      const int KR = static_cast<int>(mx_rec_k(K));
       const __amdgpu_buffer_rsrc_t s_rsrc = buffer_rsrc(
-          ssrc + ((size_t)g * N + n0) * (K / 32), static_cast<uint32_t>(qrows * (K / 32)));
+          ssrc + ((size_t)g * N + n0) / kMxRecRows * KR * kMxRecBytes,
+          static_cast<uint32_t>(qrows / kMxRecRows * KR * kMxRecBytes));
       const uint32_t q_off = static_cast<uint32_t>(qlocal) * (K / 2) + qhalf * 16;
-      const uint32_t s_off = static_cast<uint32_t>(qlocal) * (K / 32) + qhalf;
+      const uint32_t s_off = static_cast<uint32_t>(qlocal / kMxRecRows) * KR * kMxRecBytes +
+                             static_cast<uint32_t>(qlocal % kMxRecRows) * kMxRecBlocks + qhalf;
       u32x4 rq[2];
       uint32_t rs[2];
 #define MOE_FETCHQ(kt, P)                                                               \
@@ -339,7 +344,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
     _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
         ra[P][i] = load16(a_rsrc, a_off[i], k0_);                                       \
     rq[P] = load16<kStream>(q_rsrc, q_off, (kt) * 32);                                  \
-    rs[P] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, s_off, (kt) * 2, 0);            \
+    rs[P] = __builtin_amdgcn_raw_buffer_load_b8(                                        \
+        s_rsrc, s_off, ((kt) >> 2) * kMxRecBytes + 2 * ((kt) & 3), 0);                  \
   } while (0)
 #define MOE_STOREQ(kt, P)                                                               \
   do {                                                                                  \
@@ -467,11 +473,11 @@ void grouped_gemm_skinny_kernel(
     const uint16_t* __restrict__ b0,         // bf16 B: MODE 0 gate, MODE 1 down [., N, K]
     const uint16_t* __restrict__ b1,         // bf16 B: MODE 0 up
     const uint8_t* __restrict__ q0, const uint8_t* __restrict__ q1,   // MXFP4 codes
-    const uint8_t* __restrict__ s0, const uint8_t* __restrict__ s1,   // E8M0 scales
+    const uint8_t* __restrict__ s0, const uint8_t* __restrict__ s1,   // packed E8M0 scales
     const PlanEntry* __restrict__ plan, uint32_t* __restrict__ next_tile,
     void* __restrict__ c_out, uint32_t a_bytes, int K, int N, int T, int NT, int lda,
     int ldc, int E) {
-  // FP4: groups g < E are MXFP4 (codes [E, N, K/2], scales [E, N, K/32]) and groups
+  // FP4: groups g < E are MXFP4 (codes [E, N, K/2], packed scales) and groups
   // g >= E bf16 at index g - E of b0 / b1; otherwise every group is bf16 at index g.
   __shared__ float red[kSkWaves * kSkBlocks * 16 * 64];   // 64 KB of partial sums
   __shared__ uint32_t s_tile;
@@ -524,10 +530,13 @@ void grouped_gemm_skinny_kernel(
       // covers K elements 64 j + 32 hh + 8 u .. +8 of the chunk for A and B alike.
       const int nch = K / 128;
       const int nw = 2 * ((nch + 2 * kSkWaves - 1) / (2 * kSkWaves));
+      // Packed scales: the record of 64 B-rows x 8 MX blocks that covers chunk pair p of
+      // the tile's 64-row block s sits at (s * KR + p) * 512 from the tile's base.
+      const int KR = static_cast<int>(mx_rec_k(K));
       const size_t qbase = ((size_t)g * N + n0) * (K / 2);
-      const size_t sbase = ((size_t)g * N + n0) * (K / 32);
+      const size_t sbase = ((size_t)g * N + n0) / kMxRecRows * KR * kMxRecBytes;
       const uint32_t qbytes = static_cast<uint32_t>(kRowsPerSrc * (K / 2));
-      const uint32_t sbytes = static_cast<uint32_t>(kRowsPerSrc * (K / 32));
+      const uint32_t sbytes = static_cast<uint32_t>(kRowsPerSrc / kMxRecRows * KR * kMxRecBytes);
       const __amdgpu_buffer_rsrc_t qr0 = buffer_rsrc(q0 + qbase, qbytes);
       const __amdgpu_buffer_rsrc_t qr1 = buffer_rsrc((MODE == 0 ? q1 : q0) + qbase, qbytes);
       const __amdgpu_buffer_rsrc_t sr0 = buffer_rsrc(s0 + sbase, sbytes);
@@ -543,7 +552,7 @@ void grouped_gemm_skinny_kernel(
 #pragma unroll
       for (int e = 0; e < 2; ++e)
         w_off[e] = 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((4 * e + (lane >> 4)) & 7));
-      const uint32_t s_voff = static_cast<uint32_t>(ln) * (K / 32);
+      const uint32_t s_voff = static_cast<uint32_t>(ln) * kMxRecBlocks;
       u32x4 ra[2][8], rq[16];
       u32x2 rsp[kSkBlocks];          // scale bytes of the current pair
       uint32_t rs_hi[kSkBlocks];     // the pair's second chunk, kept past the next fetch
@@ -559,7 +568,9 @@ void grouped_gemm_skinny_kernel(
     _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                             \
       if ((P) == 0)                                                                     \
         rsp[b] = __builtin_amdgcn_raw_buffer_load_b64(                                  \
-            (MODE == 0 && b >= 2) ? sr1 : sr0, s_voff, MOE_SK_BRO(b) * (K / 32) + c_ * 4,   \
+            (MODE == 0 && b >= 2) ? sr1 : sr0, s_voff,                                  \
+            ((MOE_SK_BRO(b) >> 6) * KR + (c_ >> 1)) * kMxRecBytes +                     \
+                (MOE_SK_BRO(b) & 63) * kMxRecBlocks,                                    \
             0);                                                                         \
     }                                                                                   \
     _Pragma("unroll") for (int u = 0; u < 8; ++u)                                       \

@@ -208,17 +208,27 @@ moe_status_t do_grouped_mxfp4(const moe_config_t& c, int64_t T, const void* x,
                 stream);
 }
 
-// MXFP4 pointers: codes 16-byte aligned; shared experts' bf16 weights present iff S > 0.
+// MXFP4 pointers: codes and packed scales 16-byte aligned; shared experts' bf16 weights
+// present iff S > 0.
 moe_status_t check_mxfp4(const moe_config_t& c, const uint8_t* const* q, const void* wg_s,
                          const void* wu_s, const void* wd_s) {
   if (c.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   for (int i = 0; i < 6; ++i)
-    if (q[i] == nullptr) return MOE_ERR_ARG;
-  if (!aligned16(q[0]) || !aligned16(q[2]) || !aligned16(q[4])) return MOE_ERR_ARG;
+    if (q[i] == nullptr || !aligned16(q[i])) return MOE_ERR_ARG;
   if (c.n_shared > 0) {
     if (wg_s == nullptr || wu_s == nullptr || wd_s == nullptr) return MOE_ERR_ARG;
     if (!aligned16(wg_s) || !aligned16(wu_s) || !aligned16(wd_s)) return MOE_ERR_ARG;
   }
+  return MOE_OK;
+}
+
+// Shape of a scale tensor to pack: whole MX blocks along K, whole 64-row records along N.
+moe_status_t check_mx_dims(int64_t E, int64_t N, int64_t K) {
+  if (E <= 0 || N <= 0 || K <= 0) return MOE_ERR_ARG;
+  if (N % moe::kMxRecRows != 0 || K % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  // 32-bit byte offsets inside the GEMM kernels (one expert's scales).
+  if ((N / moe::kMxRecRows) * moe::mx_rec_k(K) * moe::kMxRecBytes >= (int64_t{1} << 31))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -407,6 +417,21 @@ moe_status_t moe_forward_mxfp4(const moe_config_t* cfg, int64_t T, const void* x
   MOE_TRY(do_grouped_mxfp4(*cfg, T, x, offsets, row_token, mx, w_gate_shared, w_up_shared,
                            w_down_shared, y, ws, stream));
   return do_combine(*cfg, T, y, slot_row, wts, residual, out, stream);
+}
+
+moe_status_t moe_mxfp4_scales_bytes(int64_t E, int64_t N, int64_t K, size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_ARG;
+  MOE_TRY(check_mx_dims(E, N, K));
+  *bytes = static_cast<size_t>(moe::mx_scales_bytes(E, N, K));
+  return MOE_OK;
+}
+
+moe_status_t moe_mxfp4_pack_scales(int64_t E, int64_t N, int64_t K, const uint8_t* scales,
+                                   uint8_t* packed, hipStream_t stream) {
+  MOE_TRY(check_mx_dims(E, N, K));
+  if (scales == nullptr || packed == nullptr || !aligned16(packed)) return MOE_ERR_ARG;
+  (void)hipGetLastError();
+  return finish(moe::launch_pack_mx_scales(scales, packed, E, N, K, stream), stream);
 }
 
 moe_status_t moe_rmsnorm(const moe_config_t* cfg, int64_t T, const void* x,

@@ -54,8 +54,25 @@ hipError_t launch_grouped_swiglu(int dtype, const void* x, const int32_t* offset
                                  float* y_rows, PlanEntry* plan, int T, int d, int I, int G,
                                  int R, hipStream_t stream);
 
-// MXFP4 routed-expert weights: codes [E, N, K/2] (element 2i in the low nibble) and E8M0
-// scales [E, N, K/32] per tensor (gate/up: N = I, K = d; down: N = d, K = I).
+// Packed MXFP4 scales: for each expert, each block of 64 rows of N and each run of 8 MX
+// blocks (256 elements) of K, a record of 64 rows x 8 E8M0 bytes (row-major); the last
+// record along K is zero-padded when K is not a multiple of 256.
+constexpr int kMxRecRows = 64;
+constexpr int kMxRecBlocks = 8;
+constexpr int kMxRecBytes = kMxRecRows * kMxRecBlocks;
+__host__ __device__ inline int64_t mx_rec_k(int64_t K) {
+  return (K / 32 + kMxRecBlocks - 1) / kMxRecBlocks;
+}
+inline int64_t mx_scales_bytes(int64_t E, int64_t N, int64_t K) {
+  return E * (N / kMxRecRows) * mx_rec_k(K) * kMxRecBytes;
+}
+
+// Row-major scales [E, N, K/32] -> the packed records (N % 64 == 0, K % 32 == 0).
+hipError_t launch_pack_mx_scales(const uint8_t* src, uint8_t* dst, int64_t E, int64_t N,
+                                 int64_t K, hipStream_t stream);
+
+// MXFP4 routed-expert weights: codes [E, N, K/2] (element 2i in the low nibble) and packed
+// E8M0 scales (above) per tensor (gate/up: N = I, K = d; down: N = d, K = I).
 struct MxWeights {
   const uint8_t *codes_gate, *scales_gate, *codes_up, *scales_up, *codes_down, *scales_down;
 };

@@ -84,6 +84,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               SZ, P],
         "moe_forward_rmsnorm": [CFG, I64, P, P, ctypes.c_float, ctypes.c_int32, P, P, P, P,
                                 P, P, P, P, P, P, P, SZ, P],
+        "moe_mxfp4_scales_bytes": [I64, I64, I64, ctypes.POINTER(SZ)],
+        "moe_mxfp4_pack_scales": [I64, I64, I64, P, P, P],
     }
     global ARGTYPES
     ARGTYPES = {name: len(args) for name, args in sigs.items()}
@@ -194,6 +196,17 @@ def moe_forward_rmsnorm(cfg, T, x, norm_gain, eps, zero_centred, w_router, sel_b
         _ptr(w_router), _ptr(sel_bias), _ptr(logit_offset), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(residual), _ptr(out), _ptr(topk_idx_out), _ptr(counts_out),
         _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_mxfp4_scales_bytes(E: int, N: int, K: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().moe_mxfp4_scales_bytes(E, N, K, ctypes.byref(out)))
+    return out.value
+
+
+def moe_mxfp4_pack_scales(E, N, K, scales, packed, stream=None):
+    _check(load_library().moe_mxfp4_pack_scales(E, N, K, _ptr(scales), _ptr(packed),
+                                                _stream(stream)))
 
 
 def moe_grouped_swiglu_mxfp4(cfg, T, x, offsets, row_token, wq_gate, ws_gate, wq_up, ws_up,

@@ -34,11 +34,26 @@ def expert_tensor_to_dev(arr: np.ndarray, torch, chunk: int = 16):
     return out
 
 
+def packed_scales_to_dev(scales: np.ndarray, torch, stream=None):
+    """Upload row-major E8M0 scales [E, N, K/32] and pack them on the device with
+    moe_mxfp4_pack_scales (the layout the MXFP4 entry points take)."""
+    E, N, KB = scales.shape
+    src = to_dev(scales, torch)
+    packed = torch.empty(M.moe_mxfp4_scales_bytes(E, N, 32 * KB), dtype=torch.uint8,
+                         device="cuda")
+    M.moe_mxfp4_pack_scales(E, N, 32 * KB, src, packed, stream)
+    torch.cuda.synchronize()
+    return packed
+
+
 def device_inputs(inputs: dict, torch) -> dict:
+    """Device copies of a workload's inputs; MXFP4 scales are packed on upload."""
     d = {}
     for k, v in inputs.items():
         if k in ("w_gate", "w_up", "w_down"):
             d[k] = expert_tensor_to_dev(v, torch)
+        elif k in ("ws_gate", "ws_up", "ws_down"):
+            d[k] = packed_scales_to_dev(v, torch)
         else:
             d[k] = to_dev(v, torch)
     return d

@@ -42,7 +42,8 @@ def test_library_exports_every_declared_function():
     assert set(names) == {"moe_status_str", "moe_workspace_size", "moe_route", "moe_permute",
                           "moe_grouped_swiglu", "moe_combine", "moe_forward", "moe_rmsnorm",
                           "moe_forward_rmsnorm", "moe_grouped_swiglu_mxfp4",
-                          "moe_forward_mxfp4"}
+                          "moe_forward_mxfp4", "moe_mxfp4_scales_bytes",
+                          "moe_mxfp4_pack_scales"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -165,7 +166,7 @@ def test_mxfp4_entry_points_validate_before_launch():
     c = CONFIGS["inkling_decode"]
     cfg = cfg_of(c)
     need = M.moe_workspace_size(cfg, c.T)
-    q = [A, A + 1, A, A + 1, A, A + 1]          # codes aligned, scales any byte address
+    q = [A, A + 16, A, A + 16, A, A + 16]       # codes and packed scales 16-byte aligned
 
     def status(fn, *args):
         with pytest.raises(M.MoEError) as ei:
@@ -179,10 +180,42 @@ def test_mxfp4_entry_points_validate_before_launch():
                   A, need) == M.MOE_ERR_ARG
     assert status(M.moe_grouped_swiglu_mxfp4, cfg, c.T, A, A, A, A + 8, *q[1:], A, A, A,
                   A, A, need) == M.MOE_ERR_ARG                  # misaligned codes
+    assert status(M.moe_grouped_swiglu_mxfp4, cfg, c.T, A, A, A, A, A + 1, *q[2:], A, A,
+                  A, A, A, need) == M.MOE_ERR_ARG               # misaligned packed scales
     assert status(M.moe_grouped_swiglu_mxfp4, cfg, c.T, A, A, A, *q, None, A, A, A, A,
                   need) == M.MOE_ERR_ARG                        # S = 2 needs shared weights
     assert status(M.moe_forward_mxfp4, cfg, c.T, A, A, None, None, *q, A, A, A, None, A,
                   None, None, A, need - 1) == M.MOE_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("E,N,K", [(1, 64, 32), (256, 3072, 6144), (256, 6144, 3072),
+                                   (16, 384, 256), (16, 256, 384), (6, 128, 128)])
+def test_mxfp4_scales_bytes(E, N, K):
+    # one 512-byte record per expert, 64 rows of N and 8 MX blocks (256 elements) of K,
+    # the last record along K zero-padded
+    records_k = -(-(K // 32) // 8)
+    assert M.moe_mxfp4_scales_bytes(E, N, K) == E * (N // 64) * records_k * 512
+    assert M.moe_mxfp4_scales_bytes(E, N, K) >= E * N * (K // 32)
+
+
+def test_mxfp4_pack_validates_before_launch():
+    def status(fn, *args, **kw):
+        with pytest.raises(M.MoEError) as ei:
+            fn(*args, **kw)
+        return ei.value.status
+
+    for E, N, K in [(0, 64, 32), (1, 0, 32), (1, 64, 0), (-1, 64, 32)]:
+        assert status(M.moe_mxfp4_scales_bytes, E, N, K) == M.MOE_ERR_ARG
+        assert status(M.moe_mxfp4_pack_scales, E, N, K, A, A, stream=0) == M.MOE_ERR_ARG
+    for E, N, K in [(1, 96, 32), (1, 64, 48), (1, 32, 256)]:
+        assert status(M.moe_mxfp4_scales_bytes, E, N, K) == M.MOE_ERR_UNSUPPORTED
+        assert status(M.moe_mxfp4_pack_scales, E, N, K, A, A,
+                      stream=0) == M.MOE_ERR_UNSUPPORTED
+    # one expert's packed scales must stay below 2 GiB (32-bit offsets in the kernels)
+    assert status(M.moe_mxfp4_scales_bytes, 1, 1 << 20, 1 << 16) == M.MOE_ERR_UNSUPPORTED
+    assert status(M.moe_mxfp4_pack_scales, 1, 64, 32, None, A, stream=0) == M.MOE_ERR_ARG
+    assert status(M.moe_mxfp4_pack_scales, 1, 64, 32, A, None, stream=0) == M.MOE_ERR_ARG
+    assert status(M.moe_mxfp4_pack_scales, 1, 64, 32, A, A + 8, stream=0) == M.MOE_ERR_ARG
 
 
 def test_zero_tokens_is_a_no_op():
