@@ -692,11 +692,22 @@ void grouped_gemm_skinny_kernel(
     // Partial sums -> LDS ([wave][block][register][lane]), then each wave adds the four
     // waves' partials of its share in wave order.  Accumulator layout: lane l, register
     // r -> B-row (l % 32), row 8 (r / 4) + 4 (l / 32) + (r % 4).
+    // Everything the epilogue derives from the lane and the tile is computed here from
+    // opaque copies, so the compiler neither hoists it out of the tile loop nor keeps it
+    // (spilled) through the K loop: a reload from scratch behind the weight stream costs
+    // a full memory round trip per use.
+    int lane_e = lane;
+    uint32_t lg_ = logical;
+    asm volatile("" : "+v"(lane_e), "+s"(lg_));
+    const int lne = lane_e & 31, lhe = lane_e >> 5;
+    const PlanEntry pe2 = plan[1 + lg_ / NT];
+    const int row0e = pe2.row0, nrowse = pe2.nrows;
+    const int n0e = static_cast<int>(lg_ % NT) * kRowsPerSrc;
     float* mine = red + wv * (kSkBlocks * 16 * 64);
 #pragma unroll
     for (int b = 0; b < kSkBlocks; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mine[(b * 16 + r) * 64 + lane] = acc[b][r];
+      for (int r = 0; r < 16; ++r) mine[(b * 16 + r) * 64 + lane_e] = acc[b][r];
     __syncthreads();
     if (MODE == 0) {
       // Wave w: h columns of block w % 2 (gate block w % 2, up block w % 2 + 2),
@@ -708,12 +719,12 @@ void grouped_gemm_skinny_kernel(
         float gs = 0.0f, us = 0.0f;
 #pragma unroll
         for (int w2 = 0; w2 < kSkWaves; ++w2) {
-          gs += red[((w2 * kSkBlocks + qb) * 16 + r) * 64 + lane];
-          us += red[((w2 * kSkBlocks + qb + 2) * 16 + r) * 64 + lane];
+          gs += red[((w2 * kSkBlocks + qb) * 16 + r) * 64 + lane_e];
+          us += red[((w2 * kSkBlocks + qb + 2) * 16 + r) * 64 + lane_e];
         }
-        const int m = 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (m < nrows)
-          store_h(h + (size_t)(row0 + m) * ldc + n0 + 32 * qb + ln, silu(gs) * us);
+        const int m = 8 * (r >> 2) + 4 * lhe + (r & 3);
+        if (m < nrowse)
+          store_h(h + (size_t)(row0e + m) * ldc + n0e + 32 * qb + lne, silu(gs) * us);
       }
     } else {
       float* y = static_cast<float*>(c_out);
@@ -722,9 +733,9 @@ void grouped_gemm_skinny_kernel(
         float ys = 0.0f;
 #pragma unroll
         for (int w2 = 0; w2 < kSkWaves; ++w2)
-          ys += red[((w2 * kSkBlocks + wv) * 16 + r) * 64 + lane];
-        const int m = 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (m < nrows) y[(size_t)(row0 + m) * ldc + n0 + 32 * wv + ln] = ys;
+          ys += red[((w2 * kSkBlocks + wv) * 16 + r) * 64 + lane_e];
+        const int m = 8 * (r >> 2) + 4 * lhe + (r & 3);
+        if (m < nrowse) y[(size_t)(row0e + m) * ldc + n0e + 32 * wv + lne] = ys;
       }
     }
     __syncthreads();
