@@ -460,10 +460,47 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
 // The 4 waves' partial 32 x 128 sums are added in LDS in wave order, then the SwiGLU
 // (gate/up) or the f32 row store (down) runs.  Tiles are taken from a counter, last plan
 // m-tile first, so the shared experts' bf16 tiles (about 4x the bytes of an MXFP4 tile)
-// start before the routed ones.
+// start before the routed ones.  A workgroup takes its next tile from the counter
+// during its current tile's last chunks and fetches the next tile's first chunk (pair)
+// while the last MFMAs and the epilogue run.
 constexpr int kSkBM = 32;                 // rows per m-tile
 constexpr int kSkWaves = 4;               // waves per workgroup (K split)
 constexpr int kSkBlocks = 4;              // 32-wide B-row blocks per tile (128 B-rows)
+
+// One m-tile of the decode tiling: group, first grouped row, rows, and the first B-row of
+// each source (gate/up: 64 gate + 64 up rows; down: 128 rows).
+struct SkTile {
+  int g, row0, nrows, n0;
+};
+
+template <int MODE>
+__device__ __forceinline__ SkTile sk_tile(const PlanEntry* __restrict__ plan, uint32_t logical,
+                                          int NT) {
+  const PlanEntry pe = plan[1 + logical / NT];
+  return SkTile{pe.group, pe.row0, pe.nrows,
+                static_cast<int>(logical % NT) * (MODE == 0 ? 64 : 128)};
+}
+
+// Byte offset of lane ln's A row; lanes past the group's rows read its last row (an MFMA
+// output row depends only on its own A row, and those rows are not stored).
+template <int MODE>
+__device__ __forceinline__ uint32_t sk_a_row(const int32_t* __restrict__ row_token,
+                                             const SkTile& tl, int ln, int T, int lda) {
+  const int lr = min(ln, tl.nrows - 1);
+  if (MODE == 0) {
+    int tok = row_token[tl.row0 + lr];
+    tok = min(max(tok, 0), T - 1);
+    return static_cast<uint32_t>(tok) * lda * 2;
+  }
+  return static_cast<uint32_t>(tl.row0 + lr) * lda * 2;
+}
+
+struct SkQSrc {   // MXFP4 codes and packed scales of a tile (gate/up: gate, up)
+  __amdgpu_buffer_rsrc_t q0, q1, s0, s1;
+};
+struct SkBSrc {   // bf16 weights of a tile (gate/up: gate, up)
+  __amdgpu_buffer_rsrc_t b0, b1;
+};
 
 template <int MODE, bool FP4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -480,7 +517,7 @@ void grouped_gemm_skinny_kernel(
   // FP4: groups g < E are MXFP4 (codes [E, N, K/2], packed scales) and groups
   // g >= E bf16 at index g - E of b0 / b1; otherwise every group is bf16 at index g.
   __shared__ float red[kSkWaves * kSkBlocks * 16 * 64];   // 64 KB of partial sums
-  __shared__ uint32_t s_tile;
+  __shared__ uint32_t s_tile[2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, lh = lane >> 5;
@@ -488,109 +525,98 @@ void grouped_gemm_skinny_kernel(
   const __amdgpu_buffer_rsrc_t a_rsrc = buffer_rsrc(a_src, a_bytes);
   constexpr int kRowsPerSrc = MODE == 0 ? 64 : 128;   // B-rows of one source per tile
 
-  for (;;) {
-    if (tid == 0) s_tile = atomicAdd(next_tile, 1u);
-    __syncthreads();
-    const uint32_t t = __builtin_amdgcn_readfirstlane(s_tile);
-    if (t >= ntiles) break;
-    const uint32_t logical = ntiles - 1 - t;
-    const PlanEntry pe = plan[1 + logical / NT];
-    const int g = pe.group, row0 = pe.row0, nrows = pe.nrows;
-    const int n0 = static_cast<int>(logical % NT) * kRowsPerSrc;
-    const bool quant = FP4 && g < E;
+  // MXFP4 B: chunks of 128 K elements (64 code bytes and 4 scale bytes per B-row).  Wave
+  // w takes the chunk pairs 8 p + 2 w, 8 p + 2 w + 1 (one 128-byte line of codes and 8
+  // scale bytes per B-row); iteration i of a wave is chunk 8 (i / 2) + 2 w + i % 2.  In
+  // the operand layout, part j of a chunk gives lane half hh of B-row n the code bytes
+  // 32 j + 16 hh .. +16, i.e. MX block 2 j + hh of the chunk; MFMA step (j, u) covers K
+  // elements 64 j + 32 hh + 8 u .. +8 of the chunk for A and B alike.  The record of 64
+  // B-rows x 8 MX blocks that holds the scales of chunk pair p of the tile's 64-row
+  // block s sits at (s * KR + p) * 512 from the tile's scale base.
+  const int nchq = K / 128;
+  const int KR = static_cast<int>(mx_rec_k(K));
+  const uint32_t qbytes = static_cast<uint32_t>(kRowsPerSrc * (K / 2));
+  const uint32_t sbytes = static_cast<uint32_t>(kRowsPerSrc / kMxRecRows * KR * kMxRecBytes);
+  // bf16 B: chunks of 64 K elements (128 bytes per B-row), wave w: chunks w, w + 4, ...
+  // MFMA step u, operand half hh covers K elements 32 hh + 8 u .. +8 of the chunk
+  // (16-byte slot 4 hh + u of the row) for A and B alike.
+  const int nchb = K / 64;
+  const uint32_t bbytes = static_cast<uint32_t>(kRowsPerSrc * K * 2);
+  // Weights are loaded coalesced: load q brings tile rows 8 q + lane / 8 (gate/up: rows
+  // 0..63 of the gate source for q < 8, of the up source for q >= 8), 16 bytes
+  // (lane % 8) of the chunk's (bf16) or chunk pair's (MXFP4) 128, and goes through this
+  // wave's 16 KB of LDS (its partial-sum area) to the MFMA layout, the 16-byte slot
+  // swizzled by (row / 2) % 8.
+  const uint32_t cq_voff = static_cast<uint32_t>(lane >> 3) * (K / 2) + 16 * (lane & 7);
+  const uint32_t cb_voff = static_cast<uint32_t>(lane >> 3) * K * 2 + 16 * (lane & 7);
+  const uint32_t s_voff = static_cast<uint32_t>(ln) * kMxRecBlocks;
+  char* stg = reinterpret_cast<char*>(red) + wv * (kSkBlocks * 16 * 64 * 4);
+  uint32_t w_off[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    w_off[e] = 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((4 * e + (lane >> 4)) & 7));
 
-    // A row of this lane; lanes past the group's rows read its last row (an MFMA output
-    // row depends only on its own A row, and those rows are not stored).
-    uint32_t a_row;
-    {
-      const int lr_ = min(ln, nrows - 1);
-      if (MODE == 0) {
-        int tok = row_token[row0 + lr_];
-        tok = min(max(tok, 0), T - 1);
-        a_row = static_cast<uint32_t>(tok) * lda * 2;
-      } else {
-        a_row = static_cast<uint32_t>(row0 + lr_) * lda * 2;
-      }
-    }
-    // B-row of this lane in block b, relative to its source's tile base: ln + bro(b).
-    // Gate/up blocks 0, 1 are gate rows and 2, 3 the up rows of the same columns.
+  auto q_src = [&](const SkTile& tl) {
+    const size_t qbase = ((size_t)tl.g * N + tl.n0) * (K / 2);
+    const size_t sbase = ((size_t)tl.g * N + tl.n0) / kMxRecRows * KR * kMxRecBytes;
+    return SkQSrc{buffer_rsrc(q0 + qbase, qbytes),
+                  buffer_rsrc((MODE == 0 ? q1 : q0) + qbase, qbytes),
+                  buffer_rsrc(s0 + sbase, sbytes),
+                  buffer_rsrc((MODE == 0 ? s1 : s0) + sbase, sbytes)};
+  };
+  auto b_src = [&](const SkTile& tl) {
+    const size_t bbase = ((size_t)(FP4 ? tl.g - E : tl.g) * N + tl.n0) * K;
+    return SkBSrc{buffer_rsrc(b0 + bbase, bbytes),
+                  buffer_rsrc((MODE == 0 ? b1 : b0) + bbase, bbytes)};
+  };
+
+  // Operand registers, double-buffered by chunk.  A tile's first chunk (pair) is fetched
+  // during the previous tile's last one (below), so the registers of its buffer 0 carry
+  // over from one tile to the next.
+  u32x4 qa[2][8], qc[16];      // MXFP4: A of a chunk, codes of a chunk pair
+  u32x2 qs[kSkBlocks];         // MXFP4: scale bytes of a chunk pair
+  u32x4 ba[2][4], bc[2][16];   // bf16: A and B of a chunk
+
+  // B-row of this lane in block b, relative to its source's tile base: ln + bro(b).
+  // Gate/up blocks 0, 1 are gate rows and 2, 3 the up rows of the same columns.
 #define MOE_SK_BRO(b) (MODE == 0 ? 32 * ((b) & 1) : 32 * (b))
-
-    f32x16 acc[kSkBlocks];
-#pragma unroll
-    for (int b = 0; b < kSkBlocks; ++b) acc[b] = f32x16{};
-
-    if (quant) {
-      // MXFP4 B: chunks of 128 K elements (64 code bytes and 4 scale bytes per B-row).
-      // Wave w takes the chunk pairs 8 p + 2 w, 8 p + 2 w + 1 (one 128-byte line of codes
-      // and 8 scale bytes per B-row); iteration i of a wave is chunk
-      // 8 (i / 2) + 2 w + i % 2.
-      // In the operand layout, part j of a chunk gives lane half hh of B-row n the code
-      // bytes 32 j + 16 hh .. +16, i.e. MX block 2 j + hh of the chunk; MFMA step (j, u)
-      // covers K elements 64 j + 32 hh + 8 u .. +8 of the chunk for A and B alike.
-      const int nch = K / 128;
-      const int nw = 2 * ((nch + 2 * kSkWaves - 1) / (2 * kSkWaves));
-      // Packed scales: the record of 64 B-rows x 8 MX blocks that covers chunk pair p of
-      // the tile's 64-row block s sits at (s * KR + p) * 512 from the tile's base.
-      const int KR = static_cast<int>(mx_rec_k(K));
-      const size_t qbase = ((size_t)g * N + n0) * (K / 2);
-      const size_t sbase = ((size_t)g * N + n0) / kMxRecRows * KR * kMxRecBytes;
-      const uint32_t qbytes = static_cast<uint32_t>(kRowsPerSrc * (K / 2));
-      const uint32_t sbytes = static_cast<uint32_t>(kRowsPerSrc / kMxRecRows * KR * kMxRecBytes);
-      const __amdgpu_buffer_rsrc_t qr0 = buffer_rsrc(q0 + qbase, qbytes);
-      const __amdgpu_buffer_rsrc_t qr1 = buffer_rsrc((MODE == 0 ? q1 : q0) + qbase, qbytes);
-      const __amdgpu_buffer_rsrc_t sr0 = buffer_rsrc(s0 + sbase, sbytes);
-      const __amdgpu_buffer_rsrc_t sr1 = buffer_rsrc((MODE == 0 ? s1 : s0) + sbase, sbytes);
-      const uint32_t a_voff = a_row + 64 * lh;
-      // Codes of a chunk pair (128 bytes per B-row) are loaded whole: load q brings tile
-      // rows 8 q + lane / 8 (gate/up: rows 0..63 of q0 for q < 8, of q1 for q >= 8), 16
-      // bytes (lane % 8), and goes through this wave's 16 KB of LDS (its partial-sum
-      // area) to the MFMA layout, the 16-byte slot swizzled by (row / 2) % 8.
-      const uint32_t cq_voff = static_cast<uint32_t>(lane >> 3) * (K / 2) + 16 * (lane & 7);
-      char* stg = reinterpret_cast<char*>(red) + wv * (kSkBlocks * 16 * 64 * 4);
-      uint32_t w_off[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        w_off[e] = 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((4 * e + (lane >> 4)) & 7));
-      const uint32_t s_voff = static_cast<uint32_t>(ln) * kMxRecBlocks;
-      u32x4 ra[2][8], rq[16];
-      u32x2 rsp[kSkBlocks];          // scale bytes of the current pair
-      uint32_t rs_hi[kSkBlocks];     // the pair's second chunk, kept past the next fetch
 #define MOE_SKQ_CHUNK(i) (8 * ((i) >> 1) + 2 * wv + ((i) & 1))
-#define MOE_SKQ_FETCH(i, P)                                                             \
+  // Codes and scales of the chunk pair that starts at iteration i (even), from SRC.
+#define MOE_SKQ_CODES(i, SRC)                                                           \
   do {                                                                                  \
-    const uint32_t c_ = static_cast<uint32_t>(min(MOE_SKQ_CHUNK(i), nch - 1));          \
-    if ((P) == 0) {                                                                     \
-      _Pragma("unroll") for (int q = 0; q < 16; ++q)                                    \
-          rq[q] = load16<kStream>((MODE == 0 && q >= 8) ? qr1 : qr0, cq_voff,           \
-                                  8 * (MODE == 0 ? (q & 7) : q) * (K / 2) + c_ * 64);   \
-    }                                                                                   \
-    _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                             \
-      if ((P) == 0)                                                                     \
-        rsp[b] = __builtin_amdgcn_raw_buffer_load_b64(                                  \
-            (MODE == 0 && b >= 2) ? sr1 : sr0, s_voff,                                  \
+    const uint32_t c_ = static_cast<uint32_t>(min(MOE_SKQ_CHUNK(i), nchq - 1));         \
+    _Pragma("unroll") for (int q = 0; q < 16; ++q)                                      \
+        qc[q] = load16<kStream>((MODE == 0 && q >= 8) ? (SRC).q1 : (SRC).q0, cq_voff,   \
+                                8 * (MODE == 0 ? (q & 7) : q) * (K / 2) + c_ * 64);     \
+    _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                               \
+        qs[b] = __builtin_amdgcn_raw_buffer_load_b64(                                   \
+            (MODE == 0 && b >= 2) ? (SRC).s1 : (SRC).s0, s_voff,                        \
             ((MOE_SK_BRO(b) >> 6) * KR + (c_ >> 1)) * kMxRecBytes +                     \
                 (MOE_SK_BRO(b) & 63) * kMxRecBlocks,                                    \
             0);                                                                         \
-    }                                                                                   \
+  } while (0)
+  // A of iteration i into qa[P], rows at AV.
+#define MOE_SKQ_ROWS(i, P, AV)                                                          \
+  do {                                                                                  \
+    const uint32_t c_ = static_cast<uint32_t>(min(MOE_SKQ_CHUNK(i), nchq - 1));         \
     _Pragma("unroll") for (int u = 0; u < 8; ++u)                                       \
-        ra[P][u] = load16(a_rsrc, a_voff, c_ * 256 + 128 * (u >> 2) + 16 * (u & 3));    \
+        qa[P][u] = load16(a_rsrc, (AV), c_ * 256 + 128 * (u >> 2) + 16 * (u & 3));      \
   } while (0)
 #define MOE_SKQ_MMA(i, P)                                                               \
   do {                                                                                  \
-    if (MOE_SKQ_CHUNK(i) < nch) {                                                       \
+    if (MOE_SKQ_CHUNK(i) < nchq) {                                                      \
       uint32_t sw_[kSkBlocks];                                                          \
       _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                           \
         if ((P) == 0) {                                                                 \
-          sw_[b] = rsp[b][0];                                                           \
-          rs_hi[b] = rsp[b][1];                                                         \
+          sw_[b] = qs[b][0];                                                            \
+          rs_hi[b] = qs[b][1];                                                          \
         } else {                                                                        \
           sw_[b] = rs_hi[b];                                                            \
         }                                                                               \
       }                                                                                 \
       if ((P) == 0) {                                                                   \
         _Pragma("unroll") for (int q = 0; q < 16; ++q)                                  \
-            *reinterpret_cast<u32x4*>(stg + 1024 * q + w_off[q & 1]) = rq[q];           \
+            *reinterpret_cast<u32x4*>(stg + 1024 * q + w_off[q & 1]) = qc[q];           \
       }                                                                                 \
       _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                   \
         u32x4 cq_[kSkBlocks];                                                           \
@@ -602,7 +628,7 @@ void grouped_gemm_skinny_kernel(
         _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                           \
             sc_[b] = mx_scale(sw_[b] >> (8 * (2 * j + lh)));                            \
         _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                 \
-          const bf16x8 fa_ = __builtin_bit_cast(bf16x8, ra[P][4 * j + u]);              \
+          const bf16x8 fa_ = __builtin_bit_cast(bf16x8, qa[P][4 * j + u]);              \
           _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                       \
             const bf16x8 fb_ =                                                          \
                 __builtin_bit_cast(bf16x8, mxfp4_chunk(cq_[b][u], sc_[b]));             \
@@ -612,58 +638,28 @@ void grouped_gemm_skinny_kernel(
       }                                                                                 \
     }                                                                                   \
   } while (0)
-      MOE_SKQ_FETCH(0, 0);
-      int i = 0;
-      for (; i + 2 < nw; i += 2) {
-        MOE_SKQ_FETCH(i + 1, 1);
-        MOE_SKQ_MMA(i, 0);
-        MOE_SKQ_FETCH(i + 2, 0);
-        MOE_SKQ_MMA(i + 1, 1);
-      }
-      MOE_SKQ_FETCH(i + 1, 1);
-      MOE_SKQ_MMA(i, 0);
-      MOE_SKQ_MMA(i + 1, 1);
-#undef MOE_SKQ_MMA
-#undef MOE_SKQ_FETCH
-#undef MOE_SKQ_CHUNK
-    } else {
-      // bf16 B: chunks of 64 K elements (128 bytes per B-row), wave w: chunks w, w + 4,
-      // ...  MFMA step u, operand half hh covers K elements 32 hh + 8 u .. +8 of the
-      // chunk (16-byte slot 4 hh + u of the row) for A and B alike.
-      const int gb = FP4 ? g - E : g;
-      const int nch = K / 64;
-      const int nw = max(2, ((nch + kSkWaves - 1) / kSkWaves + 1) & ~1);
-      const size_t bbase = ((size_t)gb * N + n0) * K;
-      const uint32_t bbytes = static_cast<uint32_t>(kRowsPerSrc * K * 2);
-      const __amdgpu_buffer_rsrc_t br0 = buffer_rsrc(b0 + bbase, bbytes);
-      const __amdgpu_buffer_rsrc_t br1 = buffer_rsrc((MODE == 0 ? b1 : b0) + bbase, bbytes);
-      const uint32_t a_voff = a_row + 64 * lh;
-      // Coalesced loads: load q brings tile rows 8 q + lane / 8 (gate/up: rows 0..63 of b0
-      // for q < 8, of b1 for q >= 8), 16 bytes (lane % 8) of the chunk's 128; the chunk
-      // goes through this wave's 16 KB of LDS to the MFMA layout (slot ^ (row / 2) % 8).
-      const uint32_t cb_voff = static_cast<uint32_t>(lane >> 3) * K * 2 + 16 * (lane & 7);
-      char* stg = reinterpret_cast<char*>(red) + wv * (kSkBlocks * 16 * 64 * 4);
-      uint32_t w_off[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        w_off[e] = 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((4 * e + (lane >> 4)) & 7));
-      u32x4 ra[2][4], rb[2][16];
-#define MOE_SKB_FETCH(i, P)                                                             \
+  // B of chunk wv + 4 i into bc[P], from SRC; A of that chunk into ba[P], rows at AV.
+#define MOE_SKB_CODES(i, P, SRC)                                                        \
   do {                                                                                  \
-    const uint32_t c_ = static_cast<uint32_t>(min(wv + kSkWaves * (i), nch - 1));       \
+    const uint32_t c_ = static_cast<uint32_t>(min(wv + kSkWaves * (i), nchb - 1));      \
     _Pragma("unroll") for (int q = 0; q < 16; ++q)                                      \
-        rb[P][q] = load16<kStream>((MODE == 0 && q >= 8) ? br1 : br0, cb_voff,          \
+        bc[P][q] = load16<kStream>((MODE == 0 && q >= 8) ? (SRC).b1 : (SRC).b0,         \
+                                   cb_voff,                                             \
                                    8 * (MODE == 0 ? (q & 7) : q) * K * 2 + c_ * 128);   \
+  } while (0)
+#define MOE_SKB_ROWS(i, P, AV)                                                          \
+  do {                                                                                  \
+    const uint32_t c_ = static_cast<uint32_t>(min(wv + kSkWaves * (i), nchb - 1));      \
     _Pragma("unroll") for (int u = 0; u < 4; ++u)                                       \
-        ra[P][u] = load16(a_rsrc, a_voff, c_ * 128 + 16 * u);                           \
+        ba[P][u] = load16(a_rsrc, (AV), c_ * 128 + 16 * u);                             \
   } while (0)
 #define MOE_SKB_MMA(i, P)                                                               \
   do {                                                                                  \
-    if (wv + kSkWaves * (i) < nch) {                                                    \
+    if (wv + kSkWaves * (i) < nchb) {                                                   \
       _Pragma("unroll") for (int q = 0; q < 16; ++q)                                    \
-          *reinterpret_cast<u32x4*>(stg + 1024 * q + w_off[q & 1]) = rb[P][q];          \
+          *reinterpret_cast<u32x4*>(stg + 1024 * q + w_off[q & 1]) = bc[P][q];          \
       _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                   \
-        const bf16x8 fa_ = __builtin_bit_cast(bf16x8, ra[P][u]);                        \
+        const bf16x8 fa_ = __builtin_bit_cast(bf16x8, ba[P][u]);                        \
         _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                           \
             acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                           \
                 fa_,                                                                    \
@@ -673,73 +669,178 @@ void grouped_gemm_skinny_kernel(
       }                                                                                 \
     }                                                                                   \
   } while (0)
-      MOE_SKB_FETCH(0, 0);
+  // The next tile: lane 0 of wave 0 takes it from the counter one chunk pair (MXFP4) or
+  // chunk (bf16) before this tile's last, and publishes it at the last one, so the wait
+  // for the counter and the first loads of the next tile overlap this tile's last MFMAs
+  // and its epilogue.  The slot alternates between tiles: the one written here was last
+  // read two tiles ago, before several barriers.
+#define MOE_SK_PUBLISH()                                                                \
+  do {                                                                                  \
+    if (tid == 0) s_tile[par ^ 1] = nxt;                                                \
+    __syncthreads();                                                                    \
+    tn = __builtin_amdgcn_readfirstlane(s_tile[par ^ 1]);                               \
+  } while (0)
+
+  // Sums of the four waves' partials and the tile's output, plus the next tile's first A
+  // rows (ROWS), once its row_token lookup has had the partial-sum exchange to land.
+  // Partial sums -> LDS ([wave][block][register][lane]), then each wave adds the four
+  // waves' partials of its share in wave order.  Accumulator layout: lane l, register r
+  // -> B-row (l % 32), row 8 (r / 4) + 4 (l / 32) + (r % 4).  Everything derived from
+  // the lane and the tile is computed here from opaque copies, so the compiler neither
+  // hoists it out of the tile loop nor keeps it (spilled) through the K loop: a reload
+  // from scratch behind the weight stream costs a full memory round trip per use.
+#define MOE_SK_EPILOGUE(ROWS)                                                           \
+  do {                                                                                  \
+    int lane_e = lane;                                                                  \
+    uint32_t lg_ = logical;                                                             \
+    asm volatile("" : "+v"(lane_e), "+s"(lg_));                                         \
+    const int lne = lane_e & 31, lhe = lane_e >> 5;                                     \
+    const SkTile te = sk_tile<MODE>(plan, lg_, NT);                                     \
+    float* mine = red + wv * (kSkBlocks * 16 * 64);                                     \
+    _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                               \
+        _Pragma("unroll") for (int r = 0; r < 16; ++r)                                  \
+            mine[(b * 16 + r) * 64 + lane_e] = acc[b][r];                               \
+    __syncthreads();                                                                    \
+    if (pre_n) ROWS(0, 0, sk_a_row<MODE>(row_token, ntl, ln, T, lda) + 64 * lh);        \
+    if (MODE == 0) {                                                                    \
+      /* Wave w: h columns of block w % 2 (gate block w % 2, up block w % 2 + 2), */    \
+      /* registers 8 (w / 2) .. +8. */                                                  \
+      uint16_t* h = static_cast<uint16_t*>(c_out);                                      \
+      const int qb = wv & 1, r0 = 8 * (wv >> 1);                                        \
+      _Pragma("unroll") for (int r = r0; r < r0 + 8; ++r) {                             \
+        float gs = 0.0f, us = 0.0f;                                                     \
+        _Pragma("unroll") for (int w2 = 0; w2 < kSkWaves; ++w2) {                       \
+          gs += red[((w2 * kSkBlocks + qb) * 16 + r) * 64 + lane_e];                    \
+          us += red[((w2 * kSkBlocks + qb + 2) * 16 + r) * 64 + lane_e];                \
+        }                                                                               \
+        const int m = 8 * (r >> 2) + 4 * lhe + (r & 3);                                 \
+        if (m < te.nrows)                                                               \
+          store_h(h + (size_t)(te.row0 + m) * ldc + te.n0 + 32 * qb + lne,              \
+                  silu(gs) * us);                                                       \
+      }                                                                                 \
+    } else {                                                                            \
+      float* y = static_cast<float*>(c_out);                                            \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                  \
+        float ys = 0.0f;                                                                \
+        _Pragma("unroll") for (int w2 = 0; w2 < kSkWaves; ++w2)                         \
+            ys += red[((w2 * kSkBlocks + wv) * 16 + r) * 64 + lane_e];                  \
+        const int m = 8 * (r >> 2) + 4 * lhe + (r & 3);                                 \
+        if (m < te.nrows) y[(size_t)(te.row0 + m) * ldc + te.n0 + 32 * wv + lne] = ys;  \
+      }                                                                                 \
+    }                                                                                   \
+    __syncthreads();                                                                    \
+  } while (0)
+
+  if (tid == 0) s_tile[0] = atomicAdd(next_tile, 1u);
+  __syncthreads();
+  uint32_t t = __builtin_amdgcn_readfirstlane(s_tile[0]);
+  int par = 0;
+  bool pre = false;   // this tile's first chunk (pair) was fetched during the previous one
+
+  // bf16 tiles: every tile of a bf16 layer; in an MXFP4 layer the shared experts' tiles,
+  // which the counter hands out before all routed (MXFP4) ones.  Each phase carries only
+  // its own operand registers from tile to tile.
+  while (t < ntiles) {
+    const uint32_t logical = ntiles - 1 - t;
+    const SkTile tl = sk_tile<MODE>(plan, logical, NT);
+    if (FP4 && tl.g < E) break;
+    const uint32_t a_voff = sk_a_row<MODE>(row_token, tl, ln, T, lda) + 64 * lh;
+    uint32_t nxt = 0, tn = 0;   // next tile (nxt: lane 0 of wave 0 only)
+    bool pre_n = false;         // its first chunk is fetched below
+    SkTile ntl{0, 0, 1, 0};
+    f32x16 acc[kSkBlocks];
+#pragma unroll
+    for (int b = 0; b < kSkBlocks; ++b) acc[b] = f32x16{};
+    const int nw = max(2, ((nchb + kSkWaves - 1) / kSkWaves + 1) & ~1);
+    const SkBSrc src = b_src(tl);
+    if (!pre) {
+      MOE_SKB_CODES(0, 0, src);
+      MOE_SKB_ROWS(0, 0, a_voff);
+    }
+    int i = 0;
+    for (; i + 2 < nw; i += 2) {
+      if (i + 4 >= nw && tid == 0) nxt = atomicAdd(next_tile, 1u);
+      MOE_SKB_CODES(i + 1, 1, src);
+      MOE_SKB_ROWS(i + 1, 1, a_voff);
+      MOE_SKB_MMA(i, 0);
+      MOE_SKB_CODES(i + 2, 0, src);
+      MOE_SKB_ROWS(i + 2, 0, a_voff);
+      MOE_SKB_MMA(i + 1, 1);
+    }
+    if (nw == 2 && tid == 0) nxt = atomicAdd(next_tile, 1u);
+    MOE_SK_PUBLISH();
+    MOE_SKB_CODES(i + 1, 1, src);
+    MOE_SKB_ROWS(i + 1, 1, a_voff);
+    MOE_SKB_MMA(i, 0);
+    if (tn < ntiles) {   // bc[0] is free once chunk i is in LDS
+      ntl = sk_tile<MODE>(plan, ntiles - 1 - tn, NT);
+      if (!FP4 || ntl.g >= E) {
+        MOE_SKB_CODES(0, 0, b_src(ntl));
+        pre_n = true;
+      }
+    }
+    MOE_SKB_MMA(i + 1, 1);
+    MOE_SK_EPILOGUE(MOE_SKB_ROWS);
+    t = tn;
+    par ^= 1;
+    pre = pre_n;
+  }
+
+  // MXFP4 tiles (every tile after them is one as well).
+  if (FP4) {
+    pre = false;
+    while (t < ntiles) {
+      const uint32_t logical = ntiles - 1 - t;
+      const SkTile tl = sk_tile<MODE>(plan, logical, NT);
+      const uint32_t a_voff = sk_a_row<MODE>(row_token, tl, ln, T, lda) + 64 * lh;
+      uint32_t nxt = 0, tn = 0;
+      bool pre_n = false;
+      SkTile ntl{0, 0, 1, 0};
+      f32x16 acc[kSkBlocks];
+#pragma unroll
+      for (int b = 0; b < kSkBlocks; ++b) acc[b] = f32x16{};
+      const int nw = 2 * ((nchq + 2 * kSkWaves - 1) / (2 * kSkWaves));
+      const SkQSrc src = q_src(tl);
+      uint32_t rs_hi[kSkBlocks];     // the pair's second chunk, kept past the next fetch
+      if (!pre) {
+        MOE_SKQ_CODES(0, src);
+        MOE_SKQ_ROWS(0, 0, a_voff);
+      }
       int i = 0;
       for (; i + 2 < nw; i += 2) {
-        MOE_SKB_FETCH(i + 1, 1);
-        MOE_SKB_MMA(i, 0);
-        MOE_SKB_FETCH(i + 2, 0);
-        MOE_SKB_MMA(i + 1, 1);
+        if (i + 4 >= nw && tid == 0) nxt = atomicAdd(next_tile, 1u);
+        MOE_SKQ_ROWS(i + 1, 1, a_voff);
+        MOE_SKQ_MMA(i, 0);
+        MOE_SKQ_CODES(i + 2, src);
+        MOE_SKQ_ROWS(i + 2, 0, a_voff);
+        MOE_SKQ_MMA(i + 1, 1);
       }
-      MOE_SKB_FETCH(i + 1, 1);
-      MOE_SKB_MMA(i, 0);
-      MOE_SKB_MMA(i + 1, 1);
-#undef MOE_SKB_MMA
-#undef MOE_SKB_FETCH
+      if (nw == 2 && tid == 0) nxt = atomicAdd(next_tile, 1u);
+      MOE_SK_PUBLISH();
+      MOE_SKQ_ROWS(i + 1, 1, a_voff);
+      MOE_SKQ_MMA(i, 0);
+      if (tn < ntiles) {   // qc and qs are free once chunk pair i is in LDS
+        ntl = sk_tile<MODE>(plan, ntiles - 1 - tn, NT);
+        MOE_SKQ_CODES(0, q_src(ntl));
+        pre_n = true;
+      }
+      MOE_SKQ_MMA(i + 1, 1);
+      MOE_SK_EPILOGUE(MOE_SKQ_ROWS);
+      t = tn;
+      par ^= 1;
+      pre = pre_n;
     }
-#undef MOE_SK_BRO
-
-    // Partial sums -> LDS ([wave][block][register][lane]), then each wave adds the four
-    // waves' partials of its share in wave order.  Accumulator layout: lane l, register
-    // r -> B-row (l % 32), row 8 (r / 4) + 4 (l / 32) + (r % 4).
-    // Everything the epilogue derives from the lane and the tile is computed here from
-    // opaque copies, so the compiler neither hoists it out of the tile loop nor keeps it
-    // (spilled) through the K loop: a reload from scratch behind the weight stream costs
-    // a full memory round trip per use.
-    int lane_e = lane;
-    uint32_t lg_ = logical;
-    asm volatile("" : "+v"(lane_e), "+s"(lg_));
-    const int lne = lane_e & 31, lhe = lane_e >> 5;
-    const PlanEntry pe2 = plan[1 + lg_ / NT];
-    const int row0e = pe2.row0, nrowse = pe2.nrows;
-    const int n0e = static_cast<int>(lg_ % NT) * kRowsPerSrc;
-    float* mine = red + wv * (kSkBlocks * 16 * 64);
-#pragma unroll
-    for (int b = 0; b < kSkBlocks; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mine[(b * 16 + r) * 64 + lane_e] = acc[b][r];
-    __syncthreads();
-    if (MODE == 0) {
-      // Wave w: h columns of block w % 2 (gate block w % 2, up block w % 2 + 2),
-      // registers 8 (w / 2) .. +8.
-      uint16_t* h = static_cast<uint16_t*>(c_out);
-      const int qb = wv & 1, r0 = 8 * (wv >> 1);
-#pragma unroll
-      for (int r = r0; r < r0 + 8; ++r) {
-        float gs = 0.0f, us = 0.0f;
-#pragma unroll
-        for (int w2 = 0; w2 < kSkWaves; ++w2) {
-          gs += red[((w2 * kSkBlocks + qb) * 16 + r) * 64 + lane_e];
-          us += red[((w2 * kSkBlocks + qb + 2) * 16 + r) * 64 + lane_e];
-        }
-        const int m = 8 * (r >> 2) + 4 * lhe + (r & 3);
-        if (m < nrowse)
-          store_h(h + (size_t)(row0e + m) * ldc + n0e + 32 * qb + lne, silu(gs) * us);
-      }
-    } else {
-      float* y = static_cast<float*>(c_out);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float ys = 0.0f;
-#pragma unroll
-        for (int w2 = 0; w2 < kSkWaves; ++w2)
-          ys += red[((w2 * kSkBlocks + wv) * 16 + r) * 64 + lane_e];
-        const int m = 8 * (r >> 2) + 4 * lhe + (r & 3);
-        if (m < nrowse) y[(size_t)(row0e + m) * ldc + n0e + 32 * wv + lne] = ys;
-      }
-    }
-    __syncthreads();
   }
+#undef MOE_SK_EPILOGUE
+#undef MOE_SK_PUBLISH
+#undef MOE_SKB_MMA
+#undef MOE_SKB_ROWS
+#undef MOE_SKB_CODES
+#undef MOE_SKQ_MMA
+#undef MOE_SKQ_ROWS
+#undef MOE_SKQ_CODES
+#undef MOE_SKQ_CHUNK
+#undef MOE_SK_BRO
 }
 
 // ---- 256 x 256 tiles (bf16 layers whose groups average at least 128 rows)
