@@ -196,8 +196,11 @@ def main():
     prefill_inputs = None
     for name in args.workload:
         c = CONFIGS[name]
-        steps = args.steps if c.T >= 1024 else max(args.steps, 50)
+        # The line's own workload times exactly --steps steps; the decode blocks beside a
+        # prefill line take at least 50 (each step is ~1 ms or less).
+        steps = args.steps if (name == args.workload[0] or c.T >= 1024) else max(args.steps, 50)
         res, inp = run(c, steps, args.warmup, torch)
+        res["steps"] = steps
         results[name] = res
         log(f"[{name}] {json.dumps(res)}")
         if name == "inkling_prefill":
@@ -207,7 +210,10 @@ def main():
     head = args.workload[0]
     c = CONFIGS[head]
     r = results[head]
-    if c.T >= 1024:
+    # The grouped step's bound: MFMA when its algorithmic intensity (FLOPs per byte of
+    # weights, x and Y_rows) is above the ridge of the two peaks, HBM below it.
+    intensity = r["grouped_tflops"] * 1e3 / r["grouped_gbs"]
+    if intensity >= PEAK_BF16_TFLOPS * 1e3 / PEAK_HBM_GBS:
         roof = {"bound": "mfma", "achieved": r["grouped_tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": r["grouped_tflops"] / PEAK_BF16_TFLOPS,
                 "traffic": profiled_traffic(head),
@@ -237,7 +243,7 @@ def main():
             continue
         d = results[name]
         line[key] = {
-            "workload": name, "T": d["T"], "tokens_per_s": d["tokens_per_s"],
+            "workload": name, "T": d["T"], "steps": d["steps"], "tokens_per_s": d["tokens_per_s"],
             "ms_per_step": d["ms_per_step"],
             "step_ms_p10_p50_p90": [d["event_ms_per_step_p10"], d["event_ms_per_step_median"],
                                     d["event_ms_per_step_p90"]],
