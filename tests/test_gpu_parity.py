@@ -69,6 +69,10 @@ SMALL = {c.name: c for c in [
     small("dec_sig_bf16", "sigmoid", "bf16", T=32, d=512, E=40, S=2, I=384, k=6, seed=32),
     small("dec_soft_bf16_ragged", "softmax", "bf16", T=7, d=256, E=16, S=0, I=128, k=4,
           seed=33).with_(S=1),
+    # decode tiles without shared experts: four gate/up chunks per wave (d = 1024), so the
+    # next tile is taken and prefetched inside the K loop
+    small("dec_soft_bf16_noshared", "softmax", "bf16", T=24, d=1024, E=32, S=0, I=256,
+          k=8, seed=38),
 ]}
 
 # Pre-norm shapes: x is the raw hidden state; the layer runs on RMSNorm(x).
@@ -105,6 +109,10 @@ MXFP4 = {c.name: c for c in [
     # several chunk pairs per wave: 16 gate/up and 10 down chunks over 4 waves
     small("mx_dec_multi", "sigmoid", "bf16", T=24, d=2048, E=16, S=1, I=1280, k=4,
           seed=37).with_(weight_format="mxfp4"),
+    # no shared experts: the decode kernel's bf16 loop takes no tile; two gate/up chunk
+    # pairs per wave (d = 2048)
+    small("mx_dec_noshared", "softmax", "bf16", T=16, d=2048, E=24, S=0, I=512, k=6,
+          seed=39).with_(weight_format="mxfp4"),
     small("mx_sig_rows", "sigmoid", "bf16", T=400, d=256, E=6, S=1, I=256, k=2,
           seed=30).with_(weight_format="mxfp4"),
     small("mx_soft", "softmax", "bf16", T=100, d=512, E=12, S=0, I=128, k=3,
