@@ -19,7 +19,8 @@ import numpy as np
 sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 
 from moe_inputs import CONFIGS  # noqa: E402
-from moe_inputs.generate import _CALIB_FILE, make_w_router, make_x, make_sel_bias, zipf_ranks  # noqa: E402
+from moe_inputs.generate import (  # noqa: E402
+    _CALIB_FILE, make_sel_bias, make_w_router, make_x, zipf_ranks)
 from oracle.moe_oracle import promote, route_sigmoid_shared, router_logits  # noqa: E402
 
 

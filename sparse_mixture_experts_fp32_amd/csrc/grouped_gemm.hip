@@ -449,20 +449,20 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
 // bound by streaming the experts' weights.  A tile is 32 rows x 128 B-rows (gate/up: 64
 // gate + 64 up rows of the same h columns; down: 128 output columns); the 4 waves of a
 // workgroup split its K range into interleaved chunks, double-buffered in registers one
-// chunk ahead, and the K loop has no barrier.  Weights are loaded coalesced (8 lanes x 16
-// bytes cover a 128-byte line of one B-row, so the L1 sends whole-line requests and does
-// one tag lookup per 64 bytes) and pass through the wave's own 16 KB of LDS to the MFMA
-// operand layout; A goes straight into registers in the operand layout.  The K order
-// inside a chunk is permuted (the product sums over K, so any order shared by A and B is
-// exact) so that an A load is 16 contiguous bytes and an MXFP4 operand is one MX block
-// (16 bytes of codes, one scale byte).  MXFP4 codes are converted to bf16 in registers.
-// Rows past the group's end load a copy of its last row (their outputs are not stored).
-// The 4 waves' partial 32 x 128 sums are added in LDS in wave order, then the SwiGLU
-// (gate/up) or the f32 row store (down) runs.  Tiles are taken from a counter, last plan
-// m-tile first, so the shared experts' bf16 tiles (about 4x the bytes of an MXFP4 tile)
-// start before the routed ones.  A workgroup takes its next tile from the counter
-// during its current tile's last chunks and fetches the next tile's first chunk (pair)
-// while the last MFMAs and the epilogue run.
+// chunk ahead, and the K loop's only barrier is at its last chunk (below).  Weights are
+// loaded coalesced (8 lanes x 16 bytes cover a 128-byte line of one B-row, so the L1
+// sends whole-line requests and does one tag lookup per 64 bytes) and pass through the
+// wave's own 16 KB of LDS to the MFMA operand layout; A goes straight into registers in
+// the operand layout.  The K order inside a chunk is permuted (the product sums over K,
+// so any order shared by A and B is exact) so that an A load is 16 contiguous bytes and
+// an MXFP4 operand is one MX block (16 bytes of codes, one scale byte).  MXFP4 codes are
+// converted to bf16 in registers.  Rows past the group's end load a copy of its last row
+// (their outputs are not stored).  The 4 waves' partial 32 x 128 sums are added in LDS
+// in wave order, then the SwiGLU (gate/up) or the f32 row store (down) runs.  Tiles are
+// taken from a counter, last plan m-tile first, so the shared experts' bf16 tiles (about
+// 4x the bytes of an MXFP4 tile) start before the routed ones.  A workgroup takes its
+// next tile from the counter during its current tile's last chunks and fetches the next
+// tile's first chunk (pair) while the last MFMAs and the epilogue run.
 constexpr int kSkBM = 32;                 // rows per m-tile
 constexpr int kSkWaves = 4;               // waves per workgroup (K split)
 constexpr int kSkBlocks = 4;              // 32-wide B-row blocks per tile (128 B-rows)
