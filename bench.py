@@ -166,7 +166,15 @@ def cpu_baseline(c, inp, n_tokens):
     O.moe_forward(c, inp, mode="bf16_flow", tokens=tokens)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f
+                          if ln.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": int(threads),
+            "usable_cores": len(os.sched_getaffinity(0)), "cpu_model": model,
             "kind": "oracle", "seconds": dt,
             "sample": f"first {len(tokens)} tokens of the {c.name} batch (T={c.T}), "
                       f"float64 NumPy oracle in bf16-flow mode, one call incl. routing "
