@@ -73,6 +73,11 @@ SMALL = {c.name: c for c in [
     # next tile is taken and prefetched inside the K loop
     small("dec_soft_bf16_noshared", "softmax", "bf16", T=24, d=1024, E=32, S=0, I=256,
           k=8, seed=38),
+    # the tiling boundaries: 33 tokens, one past the decode tiles (128-row tiles), and
+    # 256 tokens, the largest batch the one-workgroup permute takes
+    small("sig_bf16_t33", "sigmoid", "bf16", T=33, d=512, E=24, S=2, I=256, k=6, seed=40),
+    small("sig_bf16_t256", "sigmoid", "bf16", T=256, d=256, E=64, S=1, I=128, k=4,
+          seed=41),
 ]}
 
 # Pre-norm shapes: x is the raw hidden state; the layer runs on RMSNorm(x).
