@@ -34,6 +34,16 @@ def expert_tensor_to_dev(arr: np.ndarray, torch, chunk: int = 16):
     return out
 
 
+def packed_scale_order(scales: np.ndarray) -> np.ndarray:
+    """The packed-record order of row-major scales [E, N, K/32], by numpy reshapes:
+    record (e, 64-row block, 8-block run of K) holds 64 rows x 8 bytes, zero-padded."""
+    E, N, KB = scales.shape
+    KR = -(-KB // 8)
+    pad = np.zeros((E, N, 8 * KR), np.uint8)
+    pad[:, :, :KB] = scales
+    return pad.reshape(E, N // 64, 64, KR, 8).transpose(0, 1, 3, 2, 4).reshape(-1)
+
+
 def packed_scales_to_dev(scales: np.ndarray, torch, stream=None):
     """Upload row-major E8M0 scales [E, N, K/32] and pack them on the device with
     moe_mxfp4_pack_scales (the layout the MXFP4 entry points take)."""

@@ -198,6 +198,26 @@ def test_mxfp4_scales_bytes(E, N, K):
     assert M.moe_mxfp4_scales_bytes(E, N, K) >= E * N * (K // 32)
 
 
+@pytest.mark.parametrize("E,N,K", [(2, 64, 256), (3, 128, 384), (1, 192, 32)])
+def test_packed_scale_order_matches_the_header_formula(E, N, K):
+    # include/moe.h: packed[(((e * N/64 + nb) * KR + kr) * 64 + r) * 8 + j]
+    #                  = scale[e, 64 nb + r, 8 kr + j], zero where 8 kr + j >= K/32
+    from gpu_util import packed_scale_order
+    import numpy as np
+    KB, KR = K // 32, -(-(K // 32) // 8)
+    s = np.random.default_rng(E * N + K).integers(0, 256, size=(E, N, KB), dtype=np.uint8)
+    want = np.zeros(M.moe_mxfp4_scales_bytes(E, N, K), np.uint8)
+    for e in range(E):
+        for nb in range(N // 64):
+            for kr in range(KR):
+                for r in range(64):
+                    for j in range(8):
+                        if 8 * kr + j < KB:
+                            want[(((e * (N // 64) + nb) * KR + kr) * 64 + r) * 8 + j] = \
+                                s[e, 64 * nb + r, 8 * kr + j]
+    np.testing.assert_array_equal(packed_scale_order(s), want)
+
+
 def test_mxfp4_pack_validates_before_launch():
     def status(fn, *args, **kw):
         with pytest.raises(M.MoEError) as ei:

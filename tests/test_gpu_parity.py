@@ -13,7 +13,8 @@ torch = pytest.importorskip("torch")
 
 import sparse_mixture_experts_fp32_amd as M  # noqa: E402
 from gpu_util import (StagedRunner, cfg_struct, device_inputs, host_grouping,  # noqa: E402
-                      packed_scales_to_dev, run_forward, to_dev, workspace)
+                      packed_scale_order, packed_scales_to_dev, run_forward, to_dev,
+                      workspace)
 from moe_inputs import CONFIGS, MoEConfig, make_inputs  # noqa: E402
 from oracle import moe_oracle as O  # noqa: E402
 from parity import GAP, assert_outputs, check_routing, output_metrics  # noqa: E402
@@ -223,16 +224,6 @@ def test_forward_mxfp4(name):
     log(f"{name}: excluded {excl.sum()}/{c.T}, max rel {mx:.2e}, mean rel {mn:.2e}")
 
 
-def packed_order(scales: np.ndarray) -> np.ndarray:
-    """The packed-record order of row-major scales [E, N, K/32], by numpy reshapes:
-    record (e, 64-row block, 8-block run of K) holds 64 rows x 8 bytes, zero-padded."""
-    E, N, KB = scales.shape
-    KR = -(-KB // 8)
-    pad = np.zeros((E, N, 8 * KR), np.uint8)
-    pad[:, :, :KB] = scales
-    return pad.reshape(E, N // 64, 64, KR, 8).transpose(0, 1, 3, 2, 4).reshape(-1)
-
-
 @pytest.mark.parametrize("E,N,K", [(3, 64, 32), (5, 128, 384), (2, 192, 512),
                                    (4, 64, 1280), (7, 384, 256)])
 def test_mxfp4_pack_scales(E, N, K):
@@ -242,7 +233,7 @@ def test_mxfp4_pack_scales(E, N, K):
     s = rng.integers(0, 256, size=(E, N, K // 32), dtype=np.uint8)
     packed = packed_scales_to_dev(s, torch).cpu().numpy()
     assert packed.size == M.moe_mxfp4_scales_bytes(E, N, K)
-    np.testing.assert_array_equal(packed, packed_order(s))
+    np.testing.assert_array_equal(packed, packed_scale_order(s))
 
 
 @pytest.mark.parametrize("name", list(SMALL))
