@@ -86,6 +86,19 @@ def test_config_validation(bad, status):
     assert ei.value.status == status
 
 
+def test_token_count_limited_by_32_bit_row_offsets():
+    # The kernels address the grouped rows with 32-bit element offsets: T (k + S) rows of
+    # max(d, I) elements must stay within 2^31.
+    c = CONFIGS["inkling_prefill"]
+    cfg = cfg_of(c)
+    widest, A_ = max(c.d, c.I), c.k + c.S
+    t_max = (1 << 31) // widest // A_
+    assert M.moe_workspace_size(cfg, t_max) > 0
+    with pytest.raises(M.MoEError) as ei:
+        M.moe_workspace_size(cfg, t_max + 1)
+    assert ei.value.status == M.MOE_ERR_UNSUPPORTED
+
+
 def test_softmax_router_takes_ungated_shared_experts_but_no_scale():
     c = CONFIGS["qwen38"]
     # Ungated shared experts are accepted (up to 8); they add T rows each.
