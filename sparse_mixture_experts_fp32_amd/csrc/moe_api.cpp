@@ -369,8 +369,9 @@ moe_status_t moe_grouped_swiglu_mxfp4(const moe_config_t* cfg, int64_t T, const 
   MOE_TRY(check_cfg(cfg));
   MOE_TRY(check_tokens(*cfg, T));
   const uint8_t* q[6] = {wq_gate, ws_gate, wq_up, ws_up, wq_down, ws_down};
-  MOE_TRY(check_mxfp4(*cfg, q, w_gate_shared, w_up_shared, w_down_shared));
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
+  MOE_TRY(check_mxfp4(*cfg, q, w_gate_shared, w_up_shared, w_down_shared));
   if (x == nullptr || offsets == nullptr || row_token == nullptr || y_rows == nullptr)
     return MOE_ERR_ARG;
   if (!aligned16(x) || !aligned16(y_rows)) return MOE_ERR_ARG;
@@ -394,8 +395,9 @@ moe_status_t moe_forward_mxfp4(const moe_config_t* cfg, int64_t T, const void* x
   MOE_TRY(check_cfg(cfg));
   MOE_TRY(check_tokens(*cfg, T));
   const uint8_t* q[6] = {wq_gate, ws_gate, wq_up, ws_up, wq_down, ws_down};
-  MOE_TRY(check_mxfp4(*cfg, q, w_gate_shared, w_up_shared, w_down_shared));
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
+  MOE_TRY(check_mxfp4(*cfg, q, w_gate_shared, w_up_shared, w_down_shared));
   if (x == nullptr || w_router == nullptr || out == nullptr) return MOE_ERR_ARG;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(out) ||
       (residual != nullptr && !aligned16(residual)))

@@ -260,6 +260,12 @@ def test_zero_tokens_is_a_no_op():
     M.moe_permute(cfg, 0, None, None, None, None, None, None, 0, stream=0)
     M.moe_grouped_swiglu(cfg, 0, None, None, None, None, None, None, None, None, 0, stream=0)
     M.moe_combine(cfg, 0, None, None, None, None, None, stream=0)
+    M.moe_grouped_swiglu_mxfp4(cfg, 0, None, None, None, *([None] * 6), None, None, None,
+                               None, None, 0, stream=0)
+    M.moe_forward_mxfp4(cfg, 0, None, None, None, None, *([None] * 6), None, None, None,
+                        None, None, None, None, None, 0, stream=0)
+    M.moe_forward_rmsnorm(cfg, 0, None, None, 1e-6, 0, None, None, None, None, None, None,
+                          None, None, None, None, None, 0, stream=0)
 
 
 def test_config_struct_layout_matches_header():
