@@ -36,6 +36,9 @@
  *     MOE_ERR_HIP.  T = 0 is a no-op returning MOE_OK.  No C++ exception crosses the ABI.
  *   - Supported shapes: d % 256 == 0, I % 128 == 0, 1 <= k <= min(E, 32),
  *     E + S <= 1024, 0 <= S <= 8; softmax requires S == 0 and route_scale == 1.
+ *     Token counts: R = T (k + S) grouped rows with R * max(d, I) <= 2^31, and x [T, d]
+ *     and the intermediate [R, I + 64] each under 2^31 bytes in the layer's dtype
+ *     (MOE_ERR_UNSUPPORTED otherwise).
  *   - Calls that share a workspace must be ordered on one stream.  The library holds no
  *     global mutable state, so distinct streams with distinct workspaces are independent.
  */

@@ -114,9 +114,15 @@ moe_status_t check_cfg(const moe_config_t* c) {
 moe_status_t check_tokens(const moe_config_t& c, int64_t T) {
   if (T < 0) return MOE_ERR_ARG;
   const Dims m = dims_of(c, T);
+  const int64_t lim = int64_t{1} << 31;
   const int64_t widest = m.d > m.I ? m.d : m.I;
-  // 32-bit element offsets inside the kernels.
-  if (m.R > (int64_t{1} << 31) / widest) return MOE_ERR_UNSUPPORTED;
+  // 32-bit element offsets into the grouped rows inside the kernels.
+  if (m.R > lim / widest) return MOE_ERR_UNSUPPORTED;
+  // The GEMMs and the router read x [T, d] and the intermediate h [R, I + pad] through
+  // buffer resources with 32-bit sizes and byte offsets: both stay below 2^31 bytes.
+  const int64_t es = m.dtype == MOE_BF16 ? 2 : 4;
+  if (m.T > (lim - 1) / (m.d * es) || m.R > (lim - 1) / (moe::h_pitch(m.I) * es))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -86,13 +86,32 @@ def test_config_validation(bad, status):
     assert ei.value.status == status
 
 
-def test_token_count_limited_by_32_bit_row_offsets():
-    # The kernels address the grouped rows with 32-bit element offsets: T (k + S) rows of
-    # max(d, I) elements must stay within 2^31.
-    c = CONFIGS["inkling_prefill"]
-    cfg = cfg_of(c)
-    widest, A_ = max(c.d, c.I), c.k + c.S
-    t_max = (1 << 31) // widest // A_
+def _largest_tokens(d, I, A_, es):
+    # Largest T with T (k + S) max(d, I) <= 2^31 elements, T d es < 2^31 bytes (x) and
+    # T (k + S) (I + 64) es < 2^31 bytes (the padded intermediate), by direct search.
+    def fits(T):
+        R = T * A_
+        return (R * max(d, I) <= 1 << 31 and T * d * es < 1 << 31
+                and R * (I + 64) * es < 1 << 31)
+    lo, hi = 1, 1 << 40
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if fits(mid) else (lo, mid)
+    return lo
+
+
+@pytest.mark.parametrize("name,A_", [("inkling_prefill", None), ("qwen38", None),
+                                     ("tiny_fp32", 1), ("tiny_fp32", 32)])
+def test_token_count_limited_by_32_bit_offsets(name, A_):
+    # The kernels address the grouped rows with 32-bit element offsets and read x and the
+    # intermediate h through 32-bit byte ranges; the first token count past any of these
+    # limits is refused.
+    c = CONFIGS[name]
+    top_k = A_ if A_ is not None else c.k
+    n_experts = max(c.E, top_k)
+    cfg = cfg_of(c, top_k=top_k, n_experts=n_experts)
+    es = 4 if c.dtype == "f32" else 2
+    t_max = _largest_tokens(c.d, c.I, top_k + c.S, es)
     assert M.moe_workspace_size(cfg, t_max) > 0
     with pytest.raises(M.MoEError) as ei:
         M.moe_workspace_size(cfg, t_max + 1)
