@@ -51,6 +51,11 @@ constexpr int kNB = 4;                        // n-tiles per scheduling block
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// A buffer offset that fails the range check of every A buffer the launchers build
+// (each holds fewer than 2^31 bytes): such a lane's load returns zeros and makes no cache
+// access.  Were a buffer larger, the offset would still lie inside it.
+constexpr uint32_t kPastEnd = 0x80000000u;
+
 // 16 bytes per lane from buffer offset voffset + soffset straight into LDS at
 // lds_wave_base + 16 * lane (buffer_load_dwordx4 ... lds; counted by vmcnt).
 template <int POLICY = kCached>
@@ -223,7 +228,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
       } else {
         base = static_cast<uint32_t>(row0 + rr) * lda;
       }
-      a_off[i] = (base + lchunk[i & 1] * EPC) * sizeof(TE);
+      // Rows past the m-tile: an offset past the buffer (zeros, no L1 lookup); their
+      // output rows are not stored.
+      a_off[i] = row < nrows ? (base + lchunk[i & 1] * EPC) * sizeof(TE) : kPastEnd;
     }
     // gate/up: B-rows 0..127 (waves 0..3) are gate rows n0.., B-rows 128..255 (waves
     // 4..7) the up rows n0..;  down: B-rows 0..255 are w_down rows n0..
@@ -967,7 +974,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
       } else {
         base = static_cast<uint32_t>(row0 + rr) * lda;
       }
-      a_off[i] = (base + lchunk[i & 1] * EPC) * sizeof(TE);
+      // Rows past the m-tile get an offset beyond any buffer: the range check turns
+      // their loads into zeros without an L1 lookup (their output rows are not stored).
+      a_off[i] = row < nrows ? (base + lchunk[i & 1] * EPC) * sizeof(TE) : kPastEnd;
     }
     // gate/up: B-rows 0..127 are gate rows n0.., 128..255 the up rows n0..;  down: B-rows
     // 0..255 are w_down rows n0..  Block i of a loader is B-row brow0 + 8 i + lane / 8.
