@@ -1,0 +1,67 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU guard, how it reads the committed
+rocprofv3 summaries, and its algorithmic work figures."""
+import glob
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from moe_inputs import CONFIGS  # noqa: E402
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "8"})])
+def test_more_than_one_gpu_exits_with_a_message(argv, env):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv],
+                       capture_output=True, text=True, timeout=120,
+                       env={**os.environ, **env})
+    assert r.returncode == 2
+    assert r.stdout == ""
+    assert "one GPU only" in r.stderr
+
+
+def test_layer_flops_of_the_inkling_prefill_batch():
+    # 8,192 tokens, each through 6 routed + 2 shared SwiGLU experts of three 6,144 x 3,072
+    # GEMMs (2 flops per multiply-add), and a router over 256 + 2 rows of 6,144.
+    router, experts = bench.layer_flops(CONFIGS["inkling_prefill"])
+    assert experts == 7_421_703_487_488
+    assert router == 25_971_130_368
+
+
+def _summary(path, sha, traffic="3.42502e+10"):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("# summary\n\n| a | b |\n|---|---|\n\n")
+        f.write(f"- traffic_bytes_per_launch: {traffic}\n- sources_sha256: {sha}\n")
+
+
+def test_profiled_traffic_needs_the_current_kernel_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "grouped_sources_sha256", lambda: "aa11")
+    _summary(str(tmp_path / "profiles" / "grouped_swiglu_w.md"), "aa11")
+    assert bench.profiled_traffic("w") == pytest.approx(3.42502e10)
+    _summary(str(tmp_path / "profiles" / "grouped_swiglu_w.md"), "bb22")
+    assert bench.profiled_traffic("w") is None          # taken on other kernel sources
+    assert bench.profiled_traffic("missing") is None
+    _summary(str(tmp_path / "profiles" / "grouped_swiglu_w.md"), "aa11", traffic="n/a")
+    assert bench.profiled_traffic("w") is None
+
+
+def test_committed_summaries_carry_traffic_and_sources_hash():
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "grouped_swiglu_*.md")))
+    assert paths
+    for p in paths:
+        fields = {}
+        with open(p) as f:
+            for line in f:
+                if line.startswith("- ") and ": " in line:
+                    k, v = line[2:].strip().split(": ", 1)
+                    fields[k] = v
+        assert float(fields["traffic_bytes_per_launch"]) > 0, p
+        assert len(fields["sources_sha256"]) == 64, p
+        with open(p) as f:
+            assert "rocprofv3" in f.read(), p
