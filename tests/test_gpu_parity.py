@@ -349,6 +349,33 @@ def test_forward_residual_and_determinism():
     np.testing.assert_allclose(r.cpu().numpy() - a.cpu().numpy(), resid, rtol=0, atol=1e-6)
 
 
+@pytest.mark.parametrize("name,sizes", [("sig_bf16_wide", [600, 32, 100, 600, 7]),
+                                        ("mx_sig_rows", [400, 32, 100, 400, 7])])
+def test_workspace_reuse_across_tilings(name, sizes):
+    """One workspace, first filled with 0xFF bytes, serves calls whose batch sizes take
+    different tilings in turn (bf16: 32-row decode tiles up to 32 tokens, 128-row tiles
+    at 100 tokens, 256-row tiles at 600; MXFP4: decode and 128-row tiles).  Every counter
+    and plan the kernels use lives in the workspace and is rebuilt per call, so each
+    result equals, bit for bit, a call on a fresh workspace of its own size."""
+    c = SMALL[name] if name in SMALL else MXFP4[name]
+    inp, dev = inputs_of(c)
+    cfg = cfg_struct(c)
+    buf, n = workspace(cfg, max(sizes), torch)
+    buf.fill_(255)
+    torch.cuda.synchronize()
+    for t in sizes:
+        sub = dict(dev, x=dev["x"][:t])
+        got = run_forward(c, sub, torch, ws=(buf, n))
+        want = run_forward(c, sub, torch)
+        torch.cuda.synchronize()
+        for g, w, what in zip(got, want, ("out", "topk_idx", "counts")):
+            assert torch.equal(g, w), (name, t, what)
+        if t == c.T:
+            ref = O.moe_forward(c, inp, mode=mode_of(c))
+            excl = check_routing(got[1].cpu().numpy(), ref.routing, c.E)
+            assert_outputs(got[0].cpu().numpy()[~excl], ref.y[~excl], f"{name} T={t}")
+
+
 def test_zero_router_tie_rule_on_gpu():
     """W_r = 0 with softmax: all scores tie exactly; lower indices win."""
     c = SMALL["soft_bf16"]
