@@ -376,6 +376,34 @@ def test_workspace_reuse_across_tilings(name, sizes):
             assert_outputs(got[0].cpu().numpy()[~excl], ref.y[~excl], f"{name} T={t}")
 
 
+def test_concurrent_streams_with_own_workspaces():
+    """The library keeps no global mutable state: two layers enqueued on two streams (both
+    at the default priority) with their own workspaces, without ordering between them,
+    give exactly what each gives alone on the current stream."""
+    cases = [SMALL["sig_bf16_wide"], MXFP4["mx_sig_decode"], SMALL["soft_bf16"]]
+    alone = []
+    for c in cases:
+        _, dev = inputs_of(c)
+        alone.append((c, dev, [t.clone() for t in run_forward(c, dev, torch)]))
+        torch.cuda.synchronize()
+    # inputs_of keeps one workload's inputs at a time: hold every device dict here.
+    streams = [torch.cuda.Stream() for _ in cases]
+    spaces = [workspace(cfg_struct(c), c.T, torch) for c, _, _ in alone]
+    for buf, _ in spaces:
+        buf.fill_(255)
+    torch.cuda.synchronize()
+    got = []
+    for rep in range(3):
+        for (c, dev, _), s, ws in zip(alone, streams, spaces):
+            with torch.cuda.stream(s):
+                got.append(run_forward(c, dev, torch, ws=ws))
+    torch.cuda.synchronize()
+    for i, res in enumerate(got):
+        c, _, want = alone[i % len(cases)]
+        for g, w, what in zip(res, want, ("out", "topk_idx", "counts")):
+            assert torch.equal(g, w), (c.name, i // len(cases), what)
+
+
 def test_zero_router_tie_rule_on_gpu():
     """W_r = 0 with softmax: all scores tie exactly; lower indices win."""
     c = SMALL["soft_bf16"]
