@@ -404,6 +404,36 @@ def test_concurrent_streams_with_own_workspaces():
             assert torch.equal(g, w), (c.name, i // len(cases), what)
 
 
+@pytest.mark.parametrize("name", ["mx_sig_decode", "dec_sig_bf16", "sig_bf16_wide"])
+def test_graph_capture_and_replay(name):
+    """The entry points enqueue kernels only (no allocation, copy, memset or
+    synchronization), so a caller can capture a layer in a HIP graph.  Each replay, with
+    eager work and synchronizations between replays and the workspace refilled with 0xFF
+    bytes, matches the eager result bit for bit."""
+    c = SMALL[name] if name in SMALL else MXFP4[name]
+    _, dev = inputs_of(c)
+    ws = workspace(cfg_struct(c), c.T, torch)
+    want = [t.clone() for t in run_forward(c, dev, torch, ws=ws)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # a warm-up call off the capture stream
+        run_forward(c, dev, torch, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        got = run_forward(c, dev, torch, ws=ws)
+    for rep in range(4):
+        for t in got:
+            t.zero_()
+        ws[0].fill_(255)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for g, w, what in zip(got, want, ("out", "topk_idx", "counts")):
+            assert torch.equal(g, w), (name, rep, what)
+
+
 def test_zero_router_tie_rule_on_gpu():
     """W_r = 0 with softmax: all scores tie exactly; lower indices win."""
     c = SMALL["soft_bf16"]
