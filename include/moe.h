@@ -41,6 +41,10 @@
  *     (MOE_ERR_UNSUPPORTED otherwise).
  *   - Calls that share a workspace must be ordered on one stream.  The library holds no
  *     global mutable state, so distinct streams with distinct workspaces are independent.
+ *   - Every entry point only enqueues kernels on `stream` (no allocation, copy, memset or
+ *     synchronization; the counters the kernels use live in the workspace and are reset
+ *     by a kernel of the same call), so calls can be captured into a HIP graph and
+ *     replayed.
  */
 #ifndef MOE_H
 #define MOE_H
