@@ -44,7 +44,9 @@
  *   - Every entry point only enqueues kernels on `stream` (no allocation, copy, memset or
  *     synchronization; the counters the kernels use live in the workspace and are reset
  *     by a kernel of the same call), so calls can be captured into a HIP graph and
- *     replayed.
+ *     replayed.  The one exception is a debugging switch: with the environment variable
+ *     MOE_DEBUG_SYNC=1 every entry point synchronizes its stream after its launches and
+ *     reports a failed kernel as MOE_ERR_HIP.
  */
 #ifndef MOE_H
 #define MOE_H
