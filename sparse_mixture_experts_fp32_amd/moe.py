@@ -114,10 +114,17 @@ def header_functions(path: str = HEADER_PATH) -> list[str]:
 
 
 def _ptr(t):
+    """Device address of a tensor argument (None passes NULL; an int is taken as an address
+    the caller vouches for).  A tensor must live on a GPU and be contiguous: the kernels
+    read every buffer as dense row-major device memory, and a host address would fault."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError(f"expected a GPU tensor, got one on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor (dense row-major)")
     return t.data_ptr()
 
 

@@ -287,5 +287,19 @@ def test_zero_tokens_is_a_no_op():
                           None, None, None, None, None, 0, stream=0)
 
 
+def test_binding_refuses_host_and_strided_tensors():
+    # A host tensor's address handed to a kernel would fault the GPU; the binding refuses
+    # it (and non-contiguous views) before calling into the library.
+    torch = pytest.importorskip("torch")
+    c = CONFIGS["inkling_decode"]
+    cfg = cfg_of(c)
+    need = M.moe_workspace_size(cfg, c.T)
+    x = torch.zeros((c.T, c.d), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        M.moe_route(cfg, c.T, x, A, None, None, A, A, A, need, stream=0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        M.moe_combine(cfg, c.T, A, A, A, None, x.float().t(), stream=0)
+
+
 def test_config_struct_layout_matches_header():
     assert ctypes.sizeof(M.moe_config_t) == 9 * 4
