@@ -160,6 +160,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
   constexpr int EPC = 16 / sizeof(TE);  // elements per 16-byte chunk
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage];
 
+  // Each XCD walks one contiguous range of the list.  (Dealing chunks of 32 tiles to the
+  // XCDs in turn, as the 256-row tiling does, was slower here: 9.56 against 9.25 ms on
+  // the Qwen3.8 shape, whose tiles cost about the same everywhere.)
   const uint32_t ntiles = static_cast<uint32_t>(plan[0].group) * NT;
   const uint32_t xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
   const uint32_t q = ntiles / kXcds, r = ntiles % kXcds;
@@ -852,7 +855,8 @@ void grouped_gemm_skinny_kernel(
 
 // ---- 256 x 256 tiles (bf16 layers whose groups average at least 128 rows)
 //
-// Same decomposition and plan as above with 256-row m-tiles.  A 256 x 256 tile moves
+// Same plan and tile order as above with 256-row m-tiles, but the list is dealt to the
+// XCDs in chunks of 32 tiles, one chunk per phase (below).  A 256 x 256 tile moves
 // 64 KB per 64-wide K step for 2 x 256 x 256 x 64 flops, two thirds of the bytes per
 // flop of the 128 x 256 tile, so the CU's vector-memory path and the L2 keep up with
 // the MFMAs.  The K step is split into two halves, the 256 B-rows (32 KB) and the 256
@@ -889,11 +893,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
   constexpr int EPC = 8;  // bf16 elements per 16-byte chunk
   __shared__ __attribute__((aligned(1024))) char smem[kWSlots * kWHalf];
 
+  // Chunks of per_xcd consecutive tiles dealt to the XCDs in turn (chunk c on XCD c % 8),
+  // one chunk per phase.  Contiguous per-XCD ranges left the XCD that held the shared
+  // experts' full tiles ~10% more work than those holding routed groups, whose smaller
+  // tail m-tiles cost less (Inkling prefill: 8.92 -> 8.32 ms for both GEMMs).
   const uint32_t ntiles = static_cast<uint32_t>(plan[0].group) * NT;
   const uint32_t xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
-  const uint32_t q = ntiles / kXcds, r = ntiles % kXcds;
-  const uint32_t lo = xcd * q + (xcd < r ? xcd : r);
-  const uint32_t hi = lo + q + (xcd < r ? 1 : 0);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -916,18 +921,19 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
   const int KT = K * static_cast<int>(sizeof(TE)) / kRowBytes;
 
   uint32_t phase = 0;
-  for (uint32_t logical = lo + blockIdx.x / kXcds; logical < hi;
-       logical += per_xcd, ++phase) {
+  for (uint32_t logical = xcd * per_xcd + blockIdx.x / kXcds; logical < ntiles;
+       logical += kXcds * per_xcd, ++phase) {
     if (kPhaseSync && MODE == 0) {
       // The XCD's workgroups start each phase together, so the tiles of a phase stay
       // within a few K steps of each other and share their weight and row halves
-      // through the L2.  Phases 0..p hold min(32 (p + 1), hi - lo) tiles.  The wait is
-      // bounded: a workgroup that waits kSpinLimit polls goes on alone.  (Measured on
-      // the Inkling prefill shape: faster for gate/up, slower for the shorter down
-      // tiles, which run unsynchronized.)
+      // through the L2.  Phases 0..p hold 32 p tiles plus those of chunk 8 p + xcd (all
+      // 32 but in the list's last chunk).  The wait is bounded: a workgroup that waits
+      // kSpinLimit polls goes on alone.  (Measured on the Inkling prefill shape: faster
+      // for gate/up, slower for the shorter down tiles, which run unsynchronized.)
       if (tid == 0) {
         __hip_atomic_fetch_add(sync + xcd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t target = min((phase + 1) * per_xcd, hi - lo);
+        const uint32_t target =
+            phase * per_xcd + min(per_xcd, ntiles - (phase * kXcds + xcd) * per_xcd);
         for (int it = 0; it < kSpinLimit; ++it) {
           if (__hip_atomic_load(sync + xcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
               target)
