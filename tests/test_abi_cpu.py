@@ -303,3 +303,47 @@ def test_binding_refuses_host_and_strided_tensors():
 
 def test_config_struct_layout_matches_header():
     assert ctypes.sizeof(M.moe_config_t) == 9 * 4
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include "moe.h"
+int main(void) {
+  moe_config_t c = {6144, 256, 3072, 6, 2, MOE_ROUTER_SIGMOID_SHARED, MOE_BF16, 0, 8.0f};
+  size_t bytes = 0;
+  moe_status_t s = moe_workspace_size(&c, 32, &bytes);
+  printf("%d %zu\n", (int)s, bytes);
+  c.top_k = 300;   /* more than n_experts */
+  s = moe_workspace_size(&c, 32, &bytes);
+  printf("%d %s\n", (int)s, moe_status_str(s));
+  return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links():
+    # The boundary is a C ABI: a C99 translation unit includes moe.h, links libmoe.so and
+    # calls host-only entry points (no GPU needed).
+    import shutil
+    import subprocess
+    import tempfile
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.join(root, "sparse_mixture_experts_fp32_amd")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "abi.c"), os.path.join(d, "abi")
+        with open(src, "w") as f:
+            f.write(C_PROGRAM)
+        subprocess.run([gcc, "-std=c99", "-Wall", "-Werror=implicit-function-declaration",
+                        "-D__HIP_PLATFORM_AMD__", f"-I{root}/include", f"-I{rocm}/include",
+                        src, f"-L{libdir}", "-lmoe", f"-Wl,-rpath,{libdir}", "-o", exe],
+                       check=True, capture_output=True, text=True, timeout=120)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True,
+                             timeout=60).stdout.split("\n")
+    c = CONFIGS["inkling_decode"]
+    status, nbytes = map(int, out[0].split())
+    assert status == M.MOE_OK and nbytes == M.moe_workspace_size(cfg_of(c), 32)
+    assert out[1].startswith(f"{M.MOE_ERR_ARG} MOE_ERR_ARG")
