@@ -2,8 +2,8 @@
  * moe.h -- C ABI of the MI355X (gfx950) mixture-of-experts feed-forward layer.
  *
  * The layer (per token x, already normalized by the block's pre-norm):
- *   router   l = W_r x over the E routed and S shared experts ("A linear router scores
- *            ... experts": "Qwen3.8-2.4T-A95B vs Inkling", component table, router row);
+ *   router   l = W_r x over the E routed and S shared experts, a linear scoring of the
+ *            experts ("Qwen3.8-2.4T-A95B vs Inkling", component table, router row);
  *   select   either the softmax top-k router (softmax over the routed experts, keep the
  *            top k, renormalize; Qwen3.8 column of that row) or the sigmoid router with a
  *            shared-expert sink (sigmoid scores, top-k of the routed experts steered by a

@@ -7,17 +7,17 @@ no code, header, table or helper with it.
 
 What the layer computes (all citations are to the pages' component tables):
 
-* Router.  "A linear router" scores the experts (Qwen3.8-2.4T-A95B vs Inkling, component
-  table, router row).  Two routers exist:
+* Router.  A linear map of the token gives one score per expert (Qwen3.8-2.4T-A95B vs
+  Inkling, component table, router row).  Two routers exist:
     - softmax top-k router: softmax over the routed experts, keep the top k, renormalize,
       no selection bias (same row, Qwen3.8 column; k = 10 of 512 per the Qwen3.8 2.4T
       A95B atlas page, raw config fields num_experts / num_experts_per_tok);
     - sigmoid router with shared-expert sink: sigmoid scores over the routed and the
       shared experts, top-k of the routed experts steered by a per-expert selection bias,
       weights normalized jointly over the k + S active experts then multiplied by their
-      count (same row, Inkling column); each shared expert "is weighted by its own router
-      score, normalized jointly with the routed scores" (Inkling vs Gemma 4 31B, component
-      table, shared-expert row).
+      count (same row, Inkling column); a shared expert's weight is its own router
+      score, taken into the same normalization as the routed experts' scores (Inkling vs
+      Gemma 4 31B, component table, shared-expert row).
 * Shared experts of the softmax router.  In the blueprint, one or two shared experts
   run on every token (Qwen3.5-397B-A17B vs Inkling, block diagram, shared-expert box),
   and the blueprint's shared expert carries no gate, unlike Inkling's router-weighted
@@ -288,14 +288,16 @@ class OracleOut:
 
 
 def moe_forward_prenorm(cfg, inputs: dict, gain, eps: float, gain_offset: float,
-                        mode: str = "bf16_flow", tokens=None, residual=None) -> OracleOut:
+                        mode: str = "bf16_flow", tokens=None, forced_idx=None,
+                        residual=None) -> OracleOut:
     """The pre-norm block's branch: the layer applied to RMSNorm(x) (``prenorm_input``);
-    ``inputs["x"]`` holds the raw hidden states.  The residual, if given, is added to the
-    layer's output as in ``moe_forward``."""
+    ``inputs["x"]`` holds the raw hidden states.  ``forced_idx`` and the residual act as
+    in ``moe_forward``."""
     tok = np.arange(inputs["x"].shape[0]) if tokens is None else np.asarray(tokens)
     xn = np.zeros((inputs["x"].shape[0], cfg.d))
     xn[tok] = prenorm_input(cfg, inputs["x"], gain, eps, gain_offset, mode, tokens=tok)
-    return moe_forward(cfg, dict(inputs, x=xn), mode=mode, tokens=tok, residual=residual)
+    return moe_forward(cfg, dict(inputs, x=xn), mode=mode, tokens=tok,
+                       forced_idx=forced_idx, residual=residual)
 
 
 def moe_forward(cfg, inputs: dict, mode: str = "bf16_flow", tokens=None,

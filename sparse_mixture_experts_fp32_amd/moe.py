@@ -128,6 +128,51 @@ def _ptr(t):
     return t.data_ptr()
 
 
+# Element types of tensor arguments: "layer" is the config's dtype (bf16 or f32).
+_KINDS = {"f32": "float32", "i32": "int32", "u8": "uint8", "bf16": "bfloat16"}
+
+
+def _arg(t, what: str, kind: str, numel: int, cfg=None):
+    """``_ptr`` of tensor argument ``what`` after checking that its element type is
+    ``kind`` and that it holds at least ``numel`` elements (the extent the header gives
+    for this config and token count); raises ValueError otherwise.  Ints and None pass
+    unchecked, as in ``_ptr``."""
+    if t is None or isinstance(t, int):
+        return _ptr(t)
+    import torch
+    if kind == "layer":
+        kind = "bf16" if cfg.dtype == MOE_BF16 else "f32"
+    want = getattr(torch, _KINDS[kind])
+    if t.dtype != want:
+        raise ValueError(f"{what}: expected {want}, got {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{what}: holds {t.numel()} elements, the call reads {numel}")
+    return _ptr(t)
+
+
+def _ws(t, ws_bytes: int):
+    """Workspace pointer: any element type, at least ``ws_bytes`` bytes."""
+    if t is None or isinstance(t, int):
+        return _ptr(t)
+    if t.numel() * t.element_size() < ws_bytes:
+        raise ValueError(f"ws: {t.numel() * t.element_size()} bytes, ws_bytes says "
+                         f"{ws_bytes}")
+    return _ptr(t)
+
+
+class _Dims:
+    """Extents of a call's tensors (include/moe.h): T tokens, d, E, S, I, k, the k + S
+    active experts per token (A), E + S groups (G), T A grouped rows (R) and the router
+    rows (NR: E + S for the sigmoid router, E for softmax)."""
+
+    def __init__(self, cfg, T):
+        self.T, self.d, self.E, self.S = int(T), cfg.d_model, cfg.n_experts, cfg.n_shared
+        self.I, self.k = cfg.d_ff, cfg.top_k
+        self.A, self.G = self.k + self.S, self.E + self.S
+        self.R = self.T * self.A
+        self.NR = self.G if cfg.router == MOE_ROUTER_SIGMOID_SHARED else self.E
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -155,54 +200,90 @@ def moe_workspace_size(cfg: moe_config_t, T: int) -> int:
 
 def moe_route(cfg, T, x, w_router, sel_bias, logit_offset, topk_idx, weights, ws, ws_bytes,
               stream=None):
-    _check(load_library().moe_route(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router),
-                                    _ptr(sel_bias), _ptr(logit_offset), _ptr(topk_idx),
-                                    _ptr(weights), _ptr(ws), ws_bytes, _stream(stream)))
+    m = _Dims(cfg, T)
+    _check(load_library().moe_route(
+        ctypes.byref(cfg), T, _arg(x, "x", "layer", m.T * m.d, cfg),
+        _arg(w_router, "w_router", "layer", m.NR * m.d, cfg),
+        _arg(sel_bias, "sel_bias", "f32", m.E), _arg(logit_offset, "logit_offset", "f32", m.E),
+        _arg(topk_idx, "topk_idx", "i32", m.T * m.k),
+        _arg(weights, "weights", "f32", m.T * m.A), _ws(ws, ws_bytes), ws_bytes,
+        _stream(stream)))
 
 
 def moe_permute(cfg, T, topk_idx, counts, offsets, row_token, slot_row, ws, ws_bytes,
                 stream=None):
-    _check(load_library().moe_permute(ctypes.byref(cfg), T, _ptr(topk_idx), _ptr(counts),
-                                      _ptr(offsets), _ptr(row_token), _ptr(slot_row),
-                                      _ptr(ws), ws_bytes, _stream(stream)))
+    m = _Dims(cfg, T)
+    _check(load_library().moe_permute(
+        ctypes.byref(cfg), T, _arg(topk_idx, "topk_idx", "i32", m.T * m.k),
+        _arg(counts, "counts", "i32", m.G), _arg(offsets, "offsets", "i32", m.G + 1),
+        _arg(row_token, "row_token", "i32", m.R), _arg(slot_row, "slot_row", "i32", m.R),
+        _ws(ws, ws_bytes), ws_bytes, _stream(stream)))
+
+
+def _experts(cfg, m, w_gate, w_up, w_down, n):
+    """Dense expert weights of n experts: gate/up [n, I, d], down [n, d, I]."""
+    return (_arg(w_gate, "w_gate", "layer", n * m.I * m.d, cfg),
+            _arg(w_up, "w_up", "layer", n * m.I * m.d, cfg),
+            _arg(w_down, "w_down", "layer", n * m.d * m.I, cfg))
 
 
 def moe_grouped_swiglu(cfg, T, x, offsets, row_token, w_gate, w_up, w_down, y_rows, ws,
                        ws_bytes, stream=None):
-    _check(load_library().moe_grouped_swiglu(ctypes.byref(cfg), T, _ptr(x), _ptr(offsets),
-                                             _ptr(row_token), _ptr(w_gate), _ptr(w_up),
-                                             _ptr(w_down), _ptr(y_rows), _ptr(ws), ws_bytes,
-                                             _stream(stream)))
+    m = _Dims(cfg, T)
+    _check(load_library().moe_grouped_swiglu(
+        ctypes.byref(cfg), T, _arg(x, "x", "layer", m.T * m.d, cfg),
+        _arg(offsets, "offsets", "i32", m.G + 1), _arg(row_token, "row_token", "i32", m.R),
+        *_experts(cfg, m, w_gate, w_up, w_down, m.G), _arg(y_rows, "y_rows", "f32", m.R * m.d),
+        _ws(ws, ws_bytes), ws_bytes, _stream(stream)))
 
 
 def moe_combine(cfg, T, y_rows, slot_row, weights, residual, out, stream=None):
-    _check(load_library().moe_combine(ctypes.byref(cfg), T, _ptr(y_rows), _ptr(slot_row),
-                                      _ptr(weights), _ptr(residual), _ptr(out),
-                                      _stream(stream)))
+    m = _Dims(cfg, T)
+    _check(load_library().moe_combine(
+        ctypes.byref(cfg), T, _arg(y_rows, "y_rows", "f32", m.R * m.d),
+        _arg(slot_row, "slot_row", "i32", m.R), _arg(weights, "weights", "f32", m.T * m.A),
+        _arg(residual, "residual", "f32", m.T * m.d), _arg(out, "out", "f32", m.T * m.d),
+        _stream(stream)))
+
+
+def _forward_tail(cfg, m, residual, out, topk_idx_out, counts_out):
+    return (_arg(residual, "residual", "f32", m.T * m.d), _arg(out, "out", "f32", m.T * m.d),
+            _arg(topk_idx_out, "topk_idx_out", "i32", m.T * m.k),
+            _arg(counts_out, "counts_out", "i32", m.G))
 
 
 def moe_forward(cfg, T, x, w_router, sel_bias, logit_offset, w_gate, w_up, w_down, residual,
                 out, topk_idx_out, counts_out, ws, ws_bytes, stream=None):
-    _check(load_library().moe_forward(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router),
-                                      _ptr(sel_bias), _ptr(logit_offset), _ptr(w_gate),
-                                      _ptr(w_up), _ptr(w_down), _ptr(residual), _ptr(out),
-                                      _ptr(topk_idx_out), _ptr(counts_out), _ptr(ws),
-                                      ws_bytes, _stream(stream)))
+    m = _Dims(cfg, T)
+    _check(load_library().moe_forward(
+        ctypes.byref(cfg), T, _arg(x, "x", "layer", m.T * m.d, cfg),
+        _arg(w_router, "w_router", "layer", m.NR * m.d, cfg),
+        _arg(sel_bias, "sel_bias", "f32", m.E), _arg(logit_offset, "logit_offset", "f32", m.E),
+        *_experts(cfg, m, w_gate, w_up, w_down, m.G),
+        *_forward_tail(cfg, m, residual, out, topk_idx_out, counts_out),
+        _ws(ws, ws_bytes), ws_bytes, _stream(stream)))
 
 
 def moe_rmsnorm(cfg, T, x, gain, eps, zero_centred, y, stream=None):
-    _check(load_library().moe_rmsnorm(ctypes.byref(cfg), T, _ptr(x), _ptr(gain), float(eps),
-                                      int(zero_centred), _ptr(y), _stream(stream)))
+    m = _Dims(cfg, T)
+    _check(load_library().moe_rmsnorm(
+        ctypes.byref(cfg), T, _arg(x, "x", "layer", m.T * m.d, cfg),
+        _arg(gain, "gain", "layer", m.d, cfg), float(eps), int(zero_centred),
+        _arg(y, "y", "layer", m.T * m.d, cfg), _stream(stream)))
 
 
 def moe_forward_rmsnorm(cfg, T, x, norm_gain, eps, zero_centred, w_router, sel_bias,
                         logit_offset, w_gate, w_up, w_down, residual, out, topk_idx_out,
                         counts_out, ws, ws_bytes, stream=None):
+    m = _Dims(cfg, T)
     _check(load_library().moe_forward_rmsnorm(
-        ctypes.byref(cfg), T, _ptr(x), _ptr(norm_gain), float(eps), int(zero_centred),
-        _ptr(w_router), _ptr(sel_bias), _ptr(logit_offset), _ptr(w_gate), _ptr(w_up),
-        _ptr(w_down), _ptr(residual), _ptr(out), _ptr(topk_idx_out), _ptr(counts_out),
-        _ptr(ws), ws_bytes, _stream(stream)))
+        ctypes.byref(cfg), T, _arg(x, "x", "layer", m.T * m.d, cfg),
+        _arg(norm_gain, "norm_gain", "layer", m.d, cfg), float(eps), int(zero_centred),
+        _arg(w_router, "w_router", "layer", m.NR * m.d, cfg),
+        _arg(sel_bias, "sel_bias", "f32", m.E), _arg(logit_offset, "logit_offset", "f32", m.E),
+        *_experts(cfg, m, w_gate, w_up, w_down, m.G),
+        *_forward_tail(cfg, m, residual, out, topk_idx_out, counts_out),
+        _ws(ws, ws_bytes), ws_bytes, _stream(stream)))
 
 
 def moe_mxfp4_scales_bytes(E: int, N: int, K: int) -> int:
@@ -212,26 +293,48 @@ def moe_mxfp4_scales_bytes(E: int, N: int, K: int) -> int:
 
 
 def moe_mxfp4_pack_scales(E, N, K, scales, packed, stream=None):
-    _check(load_library().moe_mxfp4_pack_scales(E, N, K, _ptr(scales), _ptr(packed),
-                                                _stream(stream)))
+    nbytes = moe_mxfp4_scales_bytes(E, N, K)
+    _check(load_library().moe_mxfp4_pack_scales(
+        E, N, K, _arg(scales, "scales", "u8", E * N * (K // 32)),
+        _arg(packed, "packed", "u8", nbytes), _stream(stream)))
+
+
+def _mxfp4(cfg, m, wq_gate, ws_gate, wq_up, ws_up, wq_down, ws_down, wg_s, wu_s, wd_s):
+    """MXFP4 routed experts' codes and packed scales, then the shared experts' bf16
+    weights [S, I, d] / [S, d, I]."""
+    sgu = moe_mxfp4_scales_bytes(m.E, m.I, m.d)
+    sdn = moe_mxfp4_scales_bytes(m.E, m.d, m.I)
+    n = m.E * m.I * m.d // 2
+    return (_arg(wq_gate, "wq_gate", "u8", n), _arg(ws_gate, "ws_gate", "u8", sgu),
+            _arg(wq_up, "wq_up", "u8", n), _arg(ws_up, "ws_up", "u8", sgu),
+            _arg(wq_down, "wq_down", "u8", n), _arg(ws_down, "ws_down", "u8", sdn),
+            _arg(wg_s, "w_gate_shared", "bf16", m.S * m.I * m.d),
+            _arg(wu_s, "w_up_shared", "bf16", m.S * m.I * m.d),
+            _arg(wd_s, "w_down_shared", "bf16", m.S * m.d * m.I))
 
 
 def moe_grouped_swiglu_mxfp4(cfg, T, x, offsets, row_token, wq_gate, ws_gate, wq_up, ws_up,
                              wq_down, ws_down, w_gate_shared, w_up_shared, w_down_shared,
                              y_rows, ws, ws_bytes, stream=None):
+    m = _Dims(cfg, T)
     _check(load_library().moe_grouped_swiglu_mxfp4(
-        ctypes.byref(cfg), T, _ptr(x), _ptr(offsets), _ptr(row_token), _ptr(wq_gate),
-        _ptr(ws_gate), _ptr(wq_up), _ptr(ws_up), _ptr(wq_down), _ptr(ws_down),
-        _ptr(w_gate_shared), _ptr(w_up_shared), _ptr(w_down_shared), _ptr(y_rows),
-        _ptr(ws), ws_bytes, _stream(stream)))
+        ctypes.byref(cfg), T, _arg(x, "x", "layer", m.T * m.d, cfg),
+        _arg(offsets, "offsets", "i32", m.G + 1), _arg(row_token, "row_token", "i32", m.R),
+        *_mxfp4(cfg, m, wq_gate, ws_gate, wq_up, ws_up, wq_down, ws_down, w_gate_shared,
+                w_up_shared, w_down_shared),
+        _arg(y_rows, "y_rows", "f32", m.R * m.d), _ws(ws, ws_bytes), ws_bytes,
+        _stream(stream)))
 
 
 def moe_forward_mxfp4(cfg, T, x, w_router, sel_bias, logit_offset, wq_gate, ws_gate, wq_up,
                       ws_up, wq_down, ws_down, w_gate_shared, w_up_shared, w_down_shared,
                       residual, out, topk_idx_out, counts_out, ws, ws_bytes, stream=None):
+    m = _Dims(cfg, T)
     _check(load_library().moe_forward_mxfp4(
-        ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(sel_bias), _ptr(logit_offset),
-        _ptr(wq_gate), _ptr(ws_gate), _ptr(wq_up), _ptr(ws_up), _ptr(wq_down), _ptr(ws_down),
-        _ptr(w_gate_shared), _ptr(w_up_shared), _ptr(w_down_shared), _ptr(residual),
-        _ptr(out), _ptr(topk_idx_out), _ptr(counts_out), _ptr(ws), ws_bytes,
-        _stream(stream)))
+        ctypes.byref(cfg), T, _arg(x, "x", "layer", m.T * m.d, cfg),
+        _arg(w_router, "w_router", "layer", m.NR * m.d, cfg),
+        _arg(sel_bias, "sel_bias", "f32", m.E), _arg(logit_offset, "logit_offset", "f32", m.E),
+        *_mxfp4(cfg, m, wq_gate, ws_gate, wq_up, ws_up, wq_down, ws_down, w_gate_shared,
+                w_up_shared, w_down_shared),
+        *_forward_tail(cfg, m, residual, out, topk_idx_out, counts_out),
+        _ws(ws, ws_bytes), ws_bytes, _stream(stream)))

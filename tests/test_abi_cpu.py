@@ -301,6 +301,69 @@ def test_binding_refuses_host_and_strided_tensors():
         M.moe_combine(cfg, c.T, A, A, A, None, x.float().t(), stream=0)
 
 
+def test_binding_checks_dtype_and_extent_of_every_tensor():
+    # A tensor of the wrong element type, or shorter than the extent the header gives for
+    # the config and T, would let a kernel read past its end: the binding names the
+    # argument and raises before calling into the library.  Meta tensors carry dtype and
+    # size without memory; the other arguments are plain addresses, which pass unchecked.
+    torch = pytest.importorskip("torch")
+    c = CONFIGS["inkling_decode"]
+    cfg = cfg_of(c)
+    G, R = c.E + c.S, c.T * (c.k + c.S)
+    need = M.moe_workspace_size(cfg, c.T)
+
+    def t(shape, dt=torch.bfloat16):
+        return torch.empty(shape, dtype=dt, device="meta")
+
+    def err(match, fn, *args):
+        with pytest.raises(ValueError, match=match):
+            fn(*args, stream=0)
+
+    x = t((c.T, c.d))
+    wg, wd = t((G, c.I, c.d)), t((G, c.d, c.I))
+    err(r"^x: expected torch.bfloat16", M.moe_route, cfg, c.T, x.float(), A, None, None,
+        A, A, A, need)
+    err(r"^w_router: holds", M.moe_route, cfg, c.T, A, t((G - 1, c.d)), None, None, A, A,
+        A, need)
+    err(r"^sel_bias: expected torch.float32", M.moe_route, cfg, c.T, A, A, t((c.E,)), None,
+        A, A, A, need)
+    err(r"^weights: holds", M.moe_route, cfg, c.T, A, A, None, None, A,
+        t((c.T, c.k), torch.float32), A, need)
+    err(r"^ws: ", M.moe_route, cfg, c.T, A, A, None, None, A, A,
+        t((need - 1,), torch.uint8), need)
+    err(r"^counts: expected torch.int32", M.moe_permute, cfg, c.T, A,
+        t((G,), torch.int64), A, A, A, A, need)
+    err(r"^offsets: holds", M.moe_permute, cfg, c.T, A, A, t((G,), torch.int32), A, A, A,
+        need)
+    err(r"^w_up: holds", M.moe_grouped_swiglu, cfg, c.T, A, A, A, A, wg[:-1], A, A, A,
+        need)
+    err(r"^y_rows: expected torch.float32", M.moe_grouped_swiglu, cfg, c.T, A, A, A, A, A,
+        A, t((R, c.d)), A, need)
+    err(r"^slot_row: holds", M.moe_combine, cfg, c.T, A, t((R - 1,), torch.int32), A,
+        None, A)
+    err(r"^residual: expected torch.float32", M.moe_combine, cfg, c.T, A, A, A,
+        t((c.T, c.d)), A)
+    err(r"^w_down: holds", M.moe_forward, cfg, c.T, A, A, None, None, A, A,
+        wd[:, :, :-1], None, A, None, None, A, need)
+    err(r"^counts_out: holds", M.moe_forward, cfg, c.T, A, A, None, None, A, A, A, None, A,
+        None, t((c.E,), torch.int32), A, need)
+    err(r"^gain: expected torch.bfloat16", M.moe_rmsnorm, cfg, c.T, A,
+        t((c.d,), torch.float32), 1e-6, 0, A)
+    # MXFP4: codes [E, N, K/2] and packed scales of the header's size.
+    s = t((M.moe_mxfp4_scales_bytes(c.E, c.I, c.d) - 1,), torch.uint8)
+    err(r"^ws_up: holds", M.moe_grouped_swiglu_mxfp4, cfg, c.T, A, A, A, A, A, A, s, A, A,
+        A, A, A, A, A, need)
+    err(r"^wq_down: expected torch.uint8", M.moe_grouped_swiglu_mxfp4, cfg, c.T, A, A, A,
+        A, A, A, A, t((c.E, c.d, c.I // 2)), A, A, A, A, A, A, need)
+    err(r"^w_gate_shared: expected torch.bfloat16", M.moe_forward_mxfp4, cfg, c.T, A, A,
+        None, None, A, A, A, A, A, A, t((c.S, c.I, c.d), torch.float32), A, A, None, A,
+        None, None, A, need)
+    # Tensors of the right type and extent pass and stop at the device check.
+    err("GPU tensor", M.moe_route, cfg, c.T, x, A, None, None, A, A, A, need)
+    err("GPU tensor", M.moe_forward, cfg, c.T, A, A, None, None, wg, A, A, None, A, None,
+        None, A, need)
+
+
 def test_config_struct_layout_matches_header():
     assert ctypes.sizeof(M.moe_config_t) == 9 * 4
 
