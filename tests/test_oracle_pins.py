@@ -465,6 +465,89 @@ def test_ungated_shared_expert_adds_its_dense_output():
     np.testing.assert_allclose(with_shared.y - routed_only.y, dense, rtol=1e-9, atol=1e-12)
 
 
+def nearest_bf16_bits(v: float) -> int:
+    """Bit pattern of the bf16 value nearest to v, ties to the even pattern: the bf16
+    values around v's float32 pattern truncated to its upper 16 bits are compared with v
+    in exact rational arithmetic (no frexp / rint)."""
+    from fractions import Fraction
+    import struct
+
+    def val(bits):
+        return struct.unpack("<f", struct.pack("<I", (bits & 0xFFFF) << 16))[0]
+    hi16 = struct.unpack("<I", struct.pack("<f", v))[0] >> 16
+    sign = hi16 & 0x8000
+    mag = hi16 & 0x7FFF
+    cands = [sign | m for m in (mag - 1, mag, mag + 1) if 0 <= m < 0x7F80]
+    fv = Fraction(v)
+    return min(cands, key=lambda b: (abs(Fraction(val(b)) - fv), b & 1))
+
+
+@pytest.mark.parametrize("router,zc", [("sigmoid", False), ("softmax", True)])
+def test_prenorm_layer_is_the_layer_on_the_rounded_normalized_input(router, zc):
+    """moe_forward_prenorm: each token normalized by its RMS (plain Python sums), scaled
+    by its gain (1 + g for zero-centred gains), rounded once to the nearest bf16, and then
+    routed and run through the experts by the pure-Python per-token loop."""
+    cfg = small_cfg(router, dtype="bf16", T=6, d=8, E=6, S=2, I=5, k=2, seed=16).with_(
+        prenorm=True, norm_zero_centred=zc)
+    if router == "softmax":
+        cfg = cfg.with_(S=1)
+    inp = make_inputs(cfg)
+    off = 1.0 if zc else 0.0
+    x = O.promote(inp["x"], "bf16")
+    g = O.promote(inp["norm_gain"], "bf16")
+    xn_bits = np.zeros(x.shape, np.uint16)
+    for t in range(cfg.T):
+        rms = math.sqrt(sum(v * v for v in x[t]) / cfg.d + cfg.norm_eps)
+        for c in range(cfg.d):
+            xn_bits[t, c] = nearest_bf16_bits(x[t, c] / rms * (off + g[c]))
+    y, idx, w = per_token_reference(cfg, dict(inp, x=xn_bits), round_h=True)
+    out = O.moe_forward_prenorm(cfg, inp, inp["norm_gain"], cfg.norm_eps, off,
+                                mode="bf16_flow")
+    assert (out.routing.idx == idx).all()
+    np.testing.assert_allclose(out.routing.weights, w, rtol=1e-12)
+    np.testing.assert_allclose(out.y, y, rtol=1e-9, atol=1e-12)
+    # The same set in another order (forced routing) gives the same output.
+    forced = O.moe_forward_prenorm(cfg, inp, inp["norm_gain"], cfg.norm_eps, off,
+                                   mode="bf16_flow", forced_idx=idx[:, ::-1].copy())
+    np.testing.assert_allclose(forced.y, y, rtol=1e-9, atol=1e-12)
+
+
+def test_nearest_bf16_bits_against_torch():
+    """The bracketing rounding above agrees with torch's float32 -> bf16 conversion on
+    float32 inputs (single rounding there), ties and subnormals included."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(8)
+    v = np.concatenate([rng.standard_normal(300).astype(np.float32),
+                        np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8),
+                                  2.0 ** -130, 3 * 2.0 ** -134], np.float32)])
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([nearest_bf16_bits(float(a)) for a in v], np.uint16)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_forced_routing_takes_the_forced_set_and_its_own_weights():
+    """Forcing a different routed set: the output is the per-token definition on that set,
+    weighted by the oracle's own raw scores of the forced experts, normalized over it."""
+    cfg = small_cfg("sigmoid", T=8, E=8, S=2, k=2, seed=17)
+    inp = make_inputs(cfg)
+    r = O.route(cfg, inp["x"], inp["w_router"], inp["sel_bias"])
+    # the 3rd-ranked expert in place of the 2nd
+    order = np.argsort(-r.sel, axis=1, kind="stable")
+    forced = np.stack([order[:, 0], order[:, 2]], 1)
+    out = O.moe_forward(cfg, inp, mode="exact", forced_idx=forced)
+    x = inp["x"].astype(np.float64)
+    for t in range(cfg.T):
+        act = list(forced[t]) + list(range(cfg.E, cfg.E + cfg.S))
+        s = [r.scores[t, e] for e in act]
+        want = np.zeros(cfg.d)
+        for e, se in zip(act, s):
+            gg = inp["w_gate"][e].astype(np.float64) @ x[t]
+            uu = inp["w_up"][e].astype(np.float64) @ x[t]
+            want += cfg.route_scale * se / sum(s) * (
+                inp["w_down"][e].astype(np.float64) @ (gg * uu / (1 + np.exp(-gg))))
+        np.testing.assert_allclose(out.y[t], want, rtol=1e-9, atol=1e-12)
+
+
 def test_bf16_flow_differs_from_exact_at_the_single_rounding_point():
     """bf16-flow rounds only h; against the exact result the difference is the size of
     one bf16 rounding of h (relative 2^-9), far from zero and far below 1e-2."""
