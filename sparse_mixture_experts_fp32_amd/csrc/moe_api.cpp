@@ -249,6 +249,29 @@ moe_status_t do_combine(const moe_config_t& c, int64_t T, const float* y_rows,
 
 }  // namespace
 
+namespace moe {
+
+moe_status_t check_forward_args(const moe_config_t* cfg, int64_t T, const void* x,
+                                const void* w_router, const float* sel_bias,
+                                const void* w_gate, const void* w_up, const void* w_down,
+                                const float* residual, const float* out,
+                                size_t* ws_bytes_needed) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_tokens(*cfg, T));
+  if (ws_bytes_needed != nullptr) *ws_bytes_needed = layout_of(*cfg, T).total;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || w_router == nullptr || w_gate == nullptr || w_up == nullptr ||
+      w_down == nullptr || out == nullptr)
+    return MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned16(out) || (residual != nullptr && !aligned16(residual)))
+    return MOE_ERR_ARG;
+  if (sel_bias != nullptr && cfg->router != MOE_ROUTER_SIGMOID_SHARED) return MOE_ERR_ARG;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
 extern "C" {
 
 const char* moe_status_str(moe_status_t s) {
@@ -338,16 +361,9 @@ moe_status_t moe_forward(const moe_config_t* cfg, int64_t T, const void* x,
                          const void* w_down, const float* residual, float* out,
                          int32_t* topk_idx_out, int32_t* counts_out, void* ws,
                          size_t ws_bytes, hipStream_t stream) {
-  MOE_TRY(check_cfg(cfg));
-  MOE_TRY(check_tokens(*cfg, T));
+  MOE_TRY(moe::check_forward_args(cfg, T, x, w_router, sel_bias, w_gate, w_up, w_down,
+                                  residual, out, nullptr));
   if (T == 0) return MOE_OK;
-  if (x == nullptr || w_router == nullptr || w_gate == nullptr || w_up == nullptr ||
-      w_down == nullptr || out == nullptr)
-    return MOE_ERR_ARG;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
-      !aligned16(w_down) || !aligned16(out) || (residual != nullptr && !aligned16(residual)))
-    return MOE_ERR_ARG;
-  if (sel_bias != nullptr && cfg->router != MOE_ROUTER_SIGMOID_SHARED) return MOE_ERR_ARG;
   MOE_TRY(check_ws(*cfg, T, ws, ws_bytes));
   (void)hipGetLastError();
   const Layout L = layout_of(*cfg, T);

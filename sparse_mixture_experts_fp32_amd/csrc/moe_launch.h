@@ -6,7 +6,19 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moe.h"
+
 namespace moe {
+
+// Every argument check of moe_forward except the workspace's (moe_api.cpp): the config,
+// the token count and the pointers, in that order.  If ws_bytes_needed is not NULL and the
+// config and token count are valid, it receives moe_workspace_size's value.  T = 0 returns
+// MOE_OK after the config and token checks, before the pointer checks.
+moe_status_t check_forward_args(const moe_config_t* cfg, int64_t T, const void* x,
+                                const void* w_router, const float* sel_bias,
+                                const void* w_gate, const void* w_up, const void* w_down,
+                                const float* residual, const float* out,
+                                size_t* ws_bytes_needed);
 
 // Tile sizes of the grouped expert GEMMs, shared with the workspace planner.
 constexpr int kGemmBM = 128;        // grouped rows per tile
