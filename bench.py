@@ -5,16 +5,19 @@
 A step is one pass of the whole layer (route, group, grouped SwiGLU experts, combine)
 over one batch of seeded synthetic inputs already resident in HBM.  The headline
 workload is the Inkling-shaped prefill batch (T = 8,192), where the layer is bound by
-bf16 MFMA throughput; the Inkling-shaped decode batch (T = 32), bound by streaming the
-active experts' weights from HBM, is measured in the same run and reported in the same
-JSON line under "decode", and the same decode batch with MXFP4 routed-expert weights
-under "decode_mxfp4".  Rank 0 prints one JSON line.
+bf16 MFMA throughput; it heads the JSON line.  The same run measures the other
+workloads and reports each in the line's "configs" map: the Inkling-shaped decode batch
+(T = 32, bound by streaming the active experts' weights from HBM) in bf16 and with MXFP4
+routed-expert weights, the tiny fp32 layer, the Qwen3.8-shaped layer and the skewed
+(Zipf-offset) Inkling batch.  Rank 0 prints one JSON line.
 
 Per-stage durations come from HIP events recorded on the launch stream between the
 C-ABI calls of every timed step.  The dominant kernel work is the grouped SwiGLU step
-(m-tile plan + gate/up GEMM + down GEMM); its roofline is reported against the bf16
-MFMA peak (prefill) or the HBM peak (decode).  The CPU oracle is timed on a bounded
-token sample of the prefill workload on the host's cores as a reported baseline.
+(m-tile plan + gate/up GEMM + down GEMM); its roofline is reported against the MFMA peak
+of the layer's dtype or the HBM peak, whichever side of the ridge its algorithmic
+intensity falls on.  The CPU leg runs the oracle on the host's cores: its routing of
+every batch (which gives the count of near-tie tokens the parity rule excludes) and, as
+the reported baseline, the whole prefill batch timed.
 """
 from __future__ import annotations
 
@@ -26,11 +29,13 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
-sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 METRIC = ("MoE-layer tokens/s + % bf16 MFMA peak (prefill), % HBM BW (decode), 1 GPU")
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4,096 flop/clk x 2.4 GHz (dense; 2.5 PFLOP/s)
+PEAK_F32_TFLOPS = 157.3     # dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # HBM3E, 8 TB/s
+DEFAULT_WORKLOADS = ["inkling_prefill", "inkling_decode", "inkling_decode_mxfp4",
+                     "tiny_fp32", "qwen38", "inkling_skewed"]
 
 
 def log(*a):
@@ -75,11 +80,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", nargs="*",
-                   default=["inkling_prefill", "inkling_decode", "inkling_decode_mxfp4"])
-    p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=1024,
-                   help="tokens of the prefill batch the oracle is timed on")
+    p.add_argument("--workload", nargs="*", default=DEFAULT_WORKLOADS)
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the CPU leg (oracle routing counts and the oracle timing)")
+    p.add_argument("--cpu-sample", type=int, default=0,
+                   help="tokens of the prefill batch the oracle is timed on (0: all)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="first run one plain device-to-device copy of BYTES bytes, the "
                         "reference kernel for scaling hardware byte counters")
@@ -95,8 +100,8 @@ def layer_flops(c):
 def run(c, steps, warmup, torch):
     import numpy as np
 
-    from gpu_util import StagedRunner, device_inputs
     from moe_inputs import make_inputs
+    from sparse_mixture_experts_fp32_amd.staged import StagedRunner, device_inputs
 
     t0 = time.perf_counter()
     inp = make_inputs(c)
@@ -156,12 +161,30 @@ def run(c, steps, warmup, torch):
     return res, inp
 
 
+def cpu_gap_excluded(c, inp):
+    """CPU leg: the oracle's routing of the whole batch (float64), and the number of
+    tokens whose k-th / (k+1)-th selection-score gap is below the parity rule's
+    threshold (1e-6; 1e-4 for pre-norm layers), which the bit-exact index rule skips."""
+    import numpy as np
+
+    from oracle import moe_oracle as O
+    x = inp["x"]
+    if c.prenorm:
+        x = O.prenorm_input(c, inp["x"], inp["norm_gain"], c.norm_eps,
+                            1.0 if c.norm_zero_centred else 0.0)
+    r = O.route(c, x, inp["w_router"], inp.get("sel_bias"), inp.get("logit_offset"))
+    return int(np.sum(r.gap < (1e-4 if c.prenorm else 1e-6)))
+
+
 def cpu_baseline(c, inp, n_tokens):
+    """CPU leg: the oracle as it stands, timed on the host's cores over the first
+    n_tokens tokens of the batch (all of them when n_tokens is 0)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import moe_oracle as O
-    tokens = np.arange(min(n_tokens, c.T))
+    n = c.T if n_tokens <= 0 else min(n_tokens, c.T)
+    tokens = np.arange(n)
     t0 = time.perf_counter()
     O.moe_forward(c, inp, mode="bf16_flow", tokens=tokens)
     dt = time.perf_counter() - t0
@@ -173,12 +196,41 @@ def cpu_baseline(c, inp, n_tokens):
                           if ln.startswith("model name")), model)
     except OSError:
         pass
-    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": int(threads),
+    what = (f"the whole {c.name} batch ({c.T} tokens)" if n == c.T else
+            f"the first {n} of the {c.T} tokens of the {c.name} batch (a sample)")
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads),
             "usable_cores": len(os.sched_getaffinity(0)), "cpu_model": model,
             "kind": "oracle", "seconds": dt,
-            "sample": f"first {len(tokens)} tokens of the {c.name} batch (T={c.T}), "
-                      f"float64 NumPy oracle in bf16-flow mode, one call incl. routing "
-                      f"and per-expert float64 promotion"}
+            "sample": f"{what}: one float64 NumPy oracle call in bf16-flow mode, routing "
+                      f"and the per-expert float64 promotion of every touched expert's "
+                      f"weights included, input generation excluded"}
+
+
+def grouped_roofline(c, r, workload):
+    """Roofline of the grouped SwiGLU step: the MFMA peak of the layer's dtype when the
+    step's algorithmic intensity (FLOPs per byte of weights, x and Y_rows) lies above the
+    ridge of that peak and the HBM peak, the HBM peak below it."""
+    peak = PEAK_BF16_TFLOPS if c.dtype == "bf16" else PEAK_F32_TFLOPS
+    intensity = r["grouped_tflops"] * 1e3 / r["grouped_gbs"]
+    kernel = "grouped SwiGLU (gate/up + down GEMMs)"
+    if intensity >= peak * 1e3 / PEAK_HBM_GBS:
+        return {"bound": "mfma", "achieved": r["grouped_tflops"], "peak": peak,
+                "unit": "TFLOP/s", "frac": r["grouped_tflops"] / peak,
+                "traffic": profiled_traffic(workload), "kernel": kernel}
+    return {"bound": "hbm", "achieved": r["grouped_gbs"], "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": r["grouped_gbs"] / PEAK_HBM_GBS,
+            "traffic": profiled_traffic(workload), "kernel": kernel}
+
+
+def zipf_scale(c):
+    """The calibrated Zipf offset scale a* of a skewed workload (stored beside the input
+    generator), or None."""
+    if c.zipf_s == 0.0:
+        return None
+    path = os.path.join(ROOT, "moe_inputs", "zipf_calibration.json")
+    with open(path) as f:
+        rec = json.load(f).get(c.name)
+    return None if rec is None else {"a": rec["a"], "hot8_share": rec["hot8_share"]}
 
 
 def main():
@@ -202,67 +254,68 @@ def main():
         del src, dst
     results = {}
     prefill_inputs = None
+    head = args.workload[0]
     for name in args.workload:
         c = CONFIGS[name]
-        # The line's own workload times exactly --steps steps; the decode blocks beside a
-        # prefill line take at least 50 (each step is ~1 ms or less).
-        steps = args.steps if (name == args.workload[0] or c.T >= 1024) else max(args.steps, 50)
+        # The line's own workload times exactly --steps steps; a small batch beside it
+        # takes at least 50 (each of its steps is ~1 ms or less).
+        steps = args.steps if (name == head or c.T >= 1024) else max(args.steps, 50)
         res, inp = run(c, steps, args.warmup, torch)
         res["steps"] = steps
+        if not args.no_cpu_baseline:
+            t0 = time.perf_counter()
+            res["gap_excluded_tokens"] = cpu_gap_excluded(c, inp)
+            log(f"[{name}] oracle routing on the host: "
+                f"{res['gap_excluded_tokens']} near-tie tokens "
+                f"({time.perf_counter() - t0:.1f} s)")
         results[name] = res
         log(f"[{name}] {json.dumps(res)}")
         if name == "inkling_prefill":
             prefill_inputs = inp
-        else:
-            del inp
-    head = args.workload[0]
+        del inp
     c = CONFIGS[head]
     r = results[head]
-    # The grouped step's bound: MFMA when its algorithmic intensity (FLOPs per byte of
-    # weights, x and Y_rows) is above the ridge of the two peaks, HBM below it.
-    intensity = r["grouped_tflops"] * 1e3 / r["grouped_gbs"]
-    if intensity >= PEAK_BF16_TFLOPS * 1e3 / PEAK_HBM_GBS:
-        roof = {"bound": "mfma", "achieved": r["grouped_tflops"], "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": r["grouped_tflops"] / PEAK_BF16_TFLOPS,
-                "traffic": profiled_traffic(head),
-                "kernel": "grouped SwiGLU (gate/up + down GEMMs)"}
-    else:
-        roof = {"bound": "hbm", "achieved": r["grouped_gbs"], "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": r["grouped_gbs"] / PEAK_HBM_GBS,
-                "traffic": profiled_traffic(head),
-                "kernel": "grouped SwiGLU (gate/up + down GEMMs)"}
     line = {
         "metric": METRIC, "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if c.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": head, "T": c.T, "d": c.d, "E": c.E, "S": c.S, "I": c.I,
                    "k": c.k, "router": c.router},
-        "roofline": roof,
+        "roofline": grouped_roofline(c, r, head),
         "layer_tflops": r["layer_tflops"],
         "layer_frac_bf16_mfma": r["layer_tflops"] / PEAK_BF16_TFLOPS,
         "step_ms_p10_p50_p90": [r["event_ms_per_step_p10"], r["event_ms_per_step_median"],
                                 r["event_ms_per_step_p90"]],
         "stage_ms": r["stage_ms"],
         "touched_routed_experts": r["touched_routed_experts"],
+        "gap_excluded_tokens": r.get("gap_excluded_tokens"),
+        "configs": {},
     }
-    for key, name in (("decode", "inkling_decode"), ("decode_mxfp4", "inkling_decode_mxfp4")):
-        if name not in results or head == name:
+    for name in args.workload:
+        if name == head:
             continue
-        d = results[name]
-        line[key] = {
-            "workload": name, "T": d["T"], "steps": d["steps"], "tokens_per_s": d["tokens_per_s"],
-            "ms_per_step": d["ms_per_step"],
+        d, cc = results[name], CONFIGS[name]
+        peak = PEAK_BF16_TFLOPS if cc.dtype == "bf16" else PEAK_F32_TFLOPS
+        block = {
+            "workload": name, "T": d["T"], "d": cc.d, "E": cc.E, "S": cc.S, "I": cc.I,
+            "k": cc.k, "router": cc.router, "dtype": cc.dtype,
+            "weights": cc.weight_format, "steps": d["steps"],
+            "tokens_per_s": d["tokens_per_s"], "ms_per_step": d["ms_per_step"],
             "step_ms_p10_p50_p90": [d["event_ms_per_step_p10"], d["event_ms_per_step_median"],
                                     d["event_ms_per_step_p90"]],
             "stage_ms": d["stage_ms"],
-            "touched_routed_experts": d["touched_routed_experts"],
-            "roofline": {"bound": "hbm", "achieved": d["grouped_gbs"], "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": d["grouped_gbs"] / PEAK_HBM_GBS,
-                         "traffic": profiled_traffic(name)},
+            "layer_tflops": d["layer_tflops"], "layer_frac_mfma": d["layer_tflops"] / peak,
             "layer_alg_gbs": d["layer_alg_gbs"],
             "layer_frac_hbm": d["layer_alg_gbs"] / PEAK_HBM_GBS,
+            "roofline": grouped_roofline(cc, d, name),
+            "touched_routed_experts": d["touched_routed_experts"],
+            "max_rows_per_expert": d["max_rows_per_expert"],
+            "gap_excluded_tokens": d.get("gap_excluded_tokens"),
         }
+        if cc.zipf_s:
+            block["zipf"] = zipf_scale(cc)
+        line["configs"][name] = block
     if not args.no_cpu_baseline and prefill_inputs is not None:
         log("timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(CONFIGS["inkling_prefill"], prefill_inputs,
