@@ -238,6 +238,30 @@ moe_status_t moe_forward_mxfp4(const moe_config_t* cfg, int64_t T, const void* x
                                int32_t* counts_out, void* ws, size_t ws_bytes,
                                hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the whole layer as moe_forward, with
+ * its scratch space in a static device array inside the library instead of a caller
+ * workspace.  Arguments as in moe_forward, without ws and ws_bytes.
+ *   - Limit: moe_workspace_size(cfg, T) must not exceed MOE_STATIC_SCRATCH_BYTES (64 MiB:
+ *     up to ~230 tokens at the Inkling shape, ~160 at the Qwen3.8 shape); larger token
+ *     counts return MOE_ERR_WORKSPACE before anything is enqueued.
+ *   - Memory: each GPU the library runs on holds its own copy of the array until the
+ *     process ends.  The first call on a device looks up that copy's address (no
+ *     allocation); later calls on the device reuse it.  No call allocates or frees.
+ *   - Sharing: every call on one GPU uses that GPU's one array, so calls that overlap on
+ *     one GPU (on different streams, or from different host threads without ordering)
+ *     race and give undefined results; order them on one stream.  Each call rebuilds
+ *     every counter and plan it reads, so what an earlier call left in the array does
+ *     not matter.
+ *   - Errors: as moe_forward; MOE_ERR_HIP also if the device's array cannot be resolved. */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_forward_static(const moe_config_t* cfg, int64_t T, const void* x,
+                                const void* w_router, const float* sel_bias,
+                                const float* logit_offset, const void* w_gate,
+                                const void* w_up, const void* w_down, const float* residual,
+                                float* out, int32_t* topk_idx_out, int32_t* counts_out,
+                                hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 OBJ = os.path.join(PKG, "_build")
 
 HIP_SOURCES = ["rmsnorm.hip", "router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip",
-               "mx_scales.hip"]
+               "mx_scales.hip", "static_scratch.hip"]
 CXX_SOURCES = ["moe_api.cpp"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

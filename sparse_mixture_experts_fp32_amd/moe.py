@@ -86,6 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                 P, P, P, P, P, P, P, SZ, P],
         "moe_mxfp4_scales_bytes": [I64, I64, I64, ctypes.POINTER(SZ)],
         "moe_mxfp4_pack_scales": [I64, I64, I64, P, P, P],
+        "moe_forward_static": [CFG, I64, P, P, P, P, P, P, P, P, P, P, P, P],
     }
     global ARGTYPES
     ARGTYPES = {name: len(args) for name, args in sigs.items()}
@@ -262,6 +263,22 @@ def moe_forward(cfg, T, x, w_router, sel_bias, logit_offset, w_gate, w_up, w_dow
         *_experts(cfg, m, w_gate, w_up, w_down, m.G),
         *_forward_tail(cfg, m, residual, out, topk_idx_out, counts_out),
         _ws(ws, ws_bytes), ws_bytes, _stream(stream)))
+
+
+def moe_forward_static(cfg, T, x, w_router, sel_bias, logit_offset, w_gate, w_up, w_down,
+                       residual, out, topk_idx_out, counts_out, stream=None):
+    """moe_forward with the library's static device scratch instead of a workspace (for
+    callers that cannot allocate; at most MOE_STATIC_SCRATCH_BYTES of workspace)."""
+    m = _Dims(cfg, T)
+    _check(load_library().moe_forward_static(
+        ctypes.byref(cfg), T, _arg(x, "x", "layer", m.T * m.d, cfg),
+        _arg(w_router, "w_router", "layer", m.NR * m.d, cfg),
+        _arg(sel_bias, "sel_bias", "f32", m.E), _arg(logit_offset, "logit_offset", "f32", m.E),
+        *_experts(cfg, m, w_gate, w_up, w_down, m.G),
+        *_forward_tail(cfg, m, residual, out, topk_idx_out, counts_out), _stream(stream)))
+
+
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 def moe_rmsnorm(cfg, T, x, gain, eps, zero_centred, y, stream=None):

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_function():
                           "moe_grouped_swiglu", "moe_combine", "moe_forward", "moe_rmsnorm",
                           "moe_forward_rmsnorm", "moe_grouped_swiglu_mxfp4",
                           "moe_forward_mxfp4", "moe_mxfp4_scales_bytes",
-                          "moe_mxfp4_pack_scales"}
+                          "moe_mxfp4_pack_scales", "moe_forward_static"}
     for n in names:
         assert hasattr(lib, n), n
 
