@@ -855,8 +855,11 @@ void grouped_gemm_skinny_kernel(
 
 // ---- 256 x 256 tiles (bf16 layers whose groups average at least 128 rows)
 //
-// Same plan and tile order as above with 256-row m-tiles, but the list is dealt to the
-// XCDs in chunks of 32 tiles, one chunk per phase (below).  A 256 x 256 tile moves
+// The plan (plan_wide_kernel) lists 256-row m-tiles with the groups in descending order
+// of rows and a group's cheap last m-tile (at most 128 rows) split into a run of its own
+// after its full ones; within a run the tile order is the one above (blocks of 4 n-tiles,
+// the run's m-tiles consecutive).  The list is dealt to the XCDs in chunks of 32 tiles,
+// one chunk per phase (below), so most chunks hold m-tiles of one size.  A 256 x 256 tile moves
 // 64 KB per 64-wide K step for 2 x 256 x 256 x 64 flops, two thirds of the bytes per
 // flop of the 128 x 256 tile, so the CU's vector-memory path and the L2 keep up with
 // the MFMAs.  The K step is split into two halves, the 256 B-rows (32 KB) and the 256
@@ -876,6 +879,7 @@ constexpr bool kPhaseSync = true;
 constexpr int kWLoadWaves = 4;            // waves that issue the loads (4 or 8)
 constexpr int kWNB = 32 / kWLoadWaves;    // 1 KB blocks per loader wave per half
 constexpr int kSpinLimit = 4000;          // polls of a phase wait (~1.5 ms at most)
+
 
 template <int MODE>
 __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
@@ -943,9 +947,10 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
       }
       asm volatile("s_barrier" ::: "memory");
     }
+    // The tile's run of m-tiles (a group's full m-tiles, or its split-off tail): first
+    // m-tile and length, from the plan entry.
     const PlanEntry first = plan[1 + logical / NT];
-    const int g = first.group, gmt0 = first.pad;
-    const int mg = (offsets[g + 1] - offsets[g] + kWBM - 1) / kWBM;
+    const int g = first.group, gmt0 = first.pad & 0xffff, mg = first.pad >> 16;
     const uint32_t local = logical - static_cast<uint32_t>(gmt0) * NT;
     const int full = NT / kNB;
     int mloc, nt;
@@ -1179,6 +1184,63 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   }
 }
 
+// m-tile plan of the 256-row tilings.  plan[0].group = number of m-tiles; plan[1 + i]
+// = the i-th m-tile: group, first row, rows, and in .pad its run of m-tiles (first m-tile
+// in the low 16 bits, length in the high 16): the tiles of a run are consecutive in the
+// kernels' tile list.  SORT: groups in descending order of rows (ties: lower index
+// first), and a group's last m-tile with at most 128 rows, when it has full ones before
+// it, forms a run of its own right after them, so the 32-tile chunks that an XCD's
+// workgroups run together mostly hold m-tiles of one size.  Without SORT: groups in
+// index order, one run per group (the order of plan_kernel).
+template <bool SORT>
+__global__ __launch_bounds__(1024) void plan_wide_kernel(const int32_t* __restrict__ offsets,
+                                                         int G, PlanEntry* __restrict__ plan,
+                                                         uint32_t* __restrict__ sync) {
+  __shared__ int32_t cnt_s[1024];
+  __shared__ int32_t by_rank[1024];
+  __shared__ int32_t scan[1024];
+  const int t = threadIdx.x;
+  if (t < 4 * kSyncEntries) sync[t] = 0;
+  const int c = t < G ? offsets[t + 1] - offsets[t] : 0;
+  cnt_s[t] = c;
+  __syncthreads();
+  if (t < G) {
+    int rank = t;
+    if (SORT) {
+      rank = 0;
+      for (int j = 0; j < G; ++j) {
+        const int cj = cnt_s[j];
+        rank += (cj > c) || (cj == c && j < t);
+      }
+    }
+    by_rank[rank] = t;
+  }
+  __syncthreads();
+  const int g = t < G ? by_rank[t] : -1;   // the group at rank t
+  const int cg = t < G ? cnt_s[g] : 0;
+  const int m = (cg + kWBM - 1) / kWBM;
+  scan[t] = m;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = t >= o ? scan[t - o] : 0;
+    __syncthreads();
+    scan[t] += v;
+    __syncthreads();
+  }
+  const int start = scan[t] - m;
+  if (t == 1023) plan[0] = PlanEntry{scan[t], 0, 0, 0};
+  if (t < G && m > 0) {
+    const int r0 = offsets[g];
+    const int split = (SORT && m >= 2 && cg - (m - 1) * kWBM <= kWBM / 2) ? 1 : 0;
+    const int mf = m - split;
+    for (int i = 0; i < m; ++i) {
+      const int run0 = i < mf ? start : start + mf, runlen = i < mf ? mf : 1;
+      plan[1 + start + i] =
+          PlanEntry{g, r0 + i * kWBM, min(kWBM, cg - i * kWBM), run0 | (runlen << 16)};
+    }
+  }
+}
+
 // Decode-shaped tiling: plan of 32-row m-tiles, then the gate/up and down kernels, each
 // taking tiles from its own counter (zeroed by the plan kernel).  Two workgroups per CU.
 template <bool FP4>
@@ -1231,8 +1293,8 @@ static hipError_t launch_typed(const TE* x, const int32_t* offsets, const int32_
   if (sizeof(TE) == 2 && use_wide_tiles(1, R, G)) {
     // Groups average at least 128 rows: 256-row tiles.
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
-    hipLaunchKernelGGL(plan_kernel<kWBM>, dim3(1), dim3(1024), 0, stream, offsets, G, plan,
-                       sync);
+    hipLaunchKernelGGL(plan_wide_kernel<true>, dim3(1), dim3(1024), 0, stream,
+                       offsets, G, plan, sync);
     hipLaunchKernelGGL((grouped_gemm_wide_kernel<0>), dim3(grid), dim3(512), 0, stream, xb,
                        row_token, reinterpret_cast<const uint16_t*>(wg),
                        reinterpret_cast<const uint16_t*>(wu), offsets, plan, sync,
