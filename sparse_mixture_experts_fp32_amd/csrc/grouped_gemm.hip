@@ -468,11 +468,13 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
 // an MXFP4 operand is one MX block (16 bytes of codes, one scale byte).  MXFP4 codes are
 // converted to bf16 in registers.  Rows past the group's end load a copy of its last row
 // (their outputs are not stored).  The 4 waves' partial 32 x 128 sums are added in LDS
-// in wave order, then the SwiGLU (gate/up) or the f32 row store (down) runs.  Tiles are
-// taken from a counter, last plan m-tile first, so the shared experts' bf16 tiles (about
-// 4x the bytes of an MXFP4 tile) start before the routed ones.  A workgroup takes its
-// next tile from the counter during its current tile's last chunks and fetches the next
-// tile's first chunk (pair) while the last MFMAs and the epilogue run.
+// in wave order (only the row quads that hold rows of the group), then the SwiGLU
+// (gate/up) or the f32 row store (down) runs.  Tiles are taken last plan m-tile first, so
+// the shared experts' bf16 tiles (about 4x the bytes of an MXFP4 tile) start before the
+// routed ones: a workgroup's first tile is its index, later ones come from a counter.  A
+// workgroup takes its next tile from the counter during its current tile's last chunks
+// and fetches the next tile's first chunk (pair), and the row index of its A rows, while
+// the last MFMAs and the epilogue run.
 constexpr int kSkBM = 32;                 // rows per m-tile
 constexpr int kSkWaves = 4;               // waves per workgroup (K split)
 constexpr int kSkBlocks = 4;              // 32-wide B-row blocks per tile (128 B-rows)
@@ -491,18 +493,21 @@ __device__ __forceinline__ SkTile sk_tile(const PlanEntry* __restrict__ plan, ui
                 static_cast<int>(logical % NT) * (MODE == 0 ? 64 : 128)};
 }
 
-// Byte offset of lane ln's A row; lanes past the group's rows read its last row (an MFMA
-// output row depends only on its own A row, and those rows are not stored).
+// The A row of lane ln (MODE 0: its token, MODE 1: its grouped row); lanes past the
+// group's rows read its last row (an MFMA output row depends only on its own A row, and
+// those rows are not stored).
 template <int MODE>
-__device__ __forceinline__ uint32_t sk_a_row(const int32_t* __restrict__ row_token,
-                                             const SkTile& tl, int ln, int T, int lda) {
+__device__ __forceinline__ int sk_a_src(const int32_t* __restrict__ row_token,
+                                        const SkTile& tl, int ln) {
   const int lr = min(ln, tl.nrows - 1);
-  if (MODE == 0) {
-    int tok = row_token[tl.row0 + lr];
-    tok = min(max(tok, 0), T - 1);
-    return static_cast<uint32_t>(tok) * lda * 2;
-  }
-  return static_cast<uint32_t>(tl.row0 + lr) * lda * 2;
+  return MODE == 0 ? row_token[tl.row0 + lr] : tl.row0 + lr;
+}
+
+// Byte offset of that row.
+template <int MODE>
+__device__ __forceinline__ uint32_t sk_a_off(int src, int T, int lda) {
+  if (MODE == 0) src = min(max(src, 0), T - 1);
+  return static_cast<uint32_t>(src) * lda * 2;
 }
 
 struct SkQSrc {   // MXFP4 codes and packed scales of a tile (gate/up: gate, up)
@@ -692,13 +697,17 @@ void grouped_gemm_skinny_kernel(
   } while (0)
 
   // Sums of the four waves' partials and the tile's output, plus the next tile's first A
-  // rows (ROWS), once its row_token lookup has had the partial-sum exchange to land.
-  // Partial sums -> LDS ([wave][block][register][lane]), then each wave adds the four
-  // waves' partials of its share in wave order.  Accumulator layout: lane l, register r
-  // -> B-row (l % 32), row 8 (r / 4) + 4 (l / 32) + (r % 4).  Everything derived from
-  // the lane and the tile is computed here from opaque copies, so the compiler neither
-  // hoists it out of the tile loop nor keeps it (spilled) through the K loop: a reload
-  // from scratch behind the weight stream costs a full memory round trip per use.
+  // rows (ROWS) at n_aoff, from the row index n_src loaded before that tile's first
+  // weights: a wave's loads complete in issue order, so waiting here for that index does
+  // not wait for the weights, as a row_token lookup issued here would.  Partial sums ->
+  // LDS in quads of accumulator registers ([wave][block][quad][lane], 16 bytes per lane),
+  // then each wave adds the four waves' partials of its share in wave order.  Accumulator
+  // layout: lane l, register 4 q + j -> B-row (l % 32), row 8 q + 4 (l / 32) + j, so only
+  // the quads q < ceil(rows / 8) hold rows of the group (one quad for up to 8 rows, the
+  // usual decode group): the others are neither exchanged nor stored.  Everything derived
+  // from the lane and the tile is computed here from opaque copies, so the compiler
+  // neither hoists it out of the tile loop nor keeps it (spilled) through the K loop: a
+  // reload from scratch behind the weight stream costs a full memory round trip per use.
 #define MOE_SK_EPILOGUE(ROWS)                                                           \
   do {                                                                                  \
     int lane_e = lane;                                                                  \
@@ -706,46 +715,67 @@ void grouped_gemm_skinny_kernel(
     asm volatile("" : "+v"(lane_e), "+s"(lg_));                                         \
     const int lne = lane_e & 31, lhe = lane_e >> 5;                                     \
     const SkTile te = sk_tile<MODE>(plan, lg_, NT);                                     \
-    float* mine = red + wv * (kSkBlocks * 16 * 64);                                     \
+    const int nq = (te.nrows + 7) >> 3;                                                 \
+    f32x4* red4 = reinterpret_cast<f32x4*>(red);                                        \
+    f32x4* mine = red4 + wv * (kSkBlocks * 4 * 64);                                     \
     _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                               \
-        _Pragma("unroll") for (int r = 0; r < 16; ++r)                                  \
-            mine[(b * 16 + r) * 64 + lane_e] = acc[b][r];                               \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q)                                   \
+            if (q < nq)                                                                 \
+              mine[(b * 4 + q) * 64 + lane_e] =                                         \
+                  f32x4{acc[b][4 * q], acc[b][4 * q + 1], acc[b][4 * q + 2],            \
+                        acc[b][4 * q + 3]};                                             \
     __syncthreads();                                                                    \
-    if (pre_n) ROWS(0, 0, sk_a_row<MODE>(row_token, ntl, ln, T, lda) + 64 * lh);        \
+    if (pre_n) {                                                                        \
+      n_aoff = sk_a_off<MODE>(n_src, T, lda) + 64 * lh;                                 \
+      ROWS(0, 0, n_aoff);                                                               \
+    }                                                                                   \
     if (MODE == 0) {                                                                    \
       /* Wave w: h columns of block w % 2 (gate block w % 2, up block w % 2 + 2), */    \
-      /* registers 8 (w / 2) .. +8. */                                                  \
+      /* quads 2 (w / 2) and 2 (w / 2) + 1. */                                          \
       uint16_t* h = static_cast<uint16_t*>(c_out);                                      \
-      const int qb = wv & 1, r0 = 8 * (wv >> 1);                                        \
-      _Pragma("unroll") for (int r = r0; r < r0 + 8; ++r) {                             \
-        float gs = 0.0f, us = 0.0f;                                                     \
-        _Pragma("unroll") for (int w2 = 0; w2 < kSkWaves; ++w2) {                       \
-          gs += red[((w2 * kSkBlocks + qb) * 16 + r) * 64 + lane_e];                    \
-          us += red[((w2 * kSkBlocks + qb + 2) * 16 + r) * 64 + lane_e];                \
+      const int qb = wv & 1;                                                            \
+      _Pragma("unroll") for (int qq = 0; qq < 2; ++qq) {                                \
+        const int q = 2 * (wv >> 1) + qq;                                               \
+        if (q < nq) {                                                                   \
+          f32x4 gs = {0.0f, 0.0f, 0.0f, 0.0f}, us = gs;                                 \
+          _Pragma("unroll") for (int w2 = 0; w2 < kSkWaves; ++w2) {                     \
+            gs += red4[((w2 * kSkBlocks + qb) * 4 + q) * 64 + lane_e];                  \
+            us += red4[((w2 * kSkBlocks + qb + 2) * 4 + q) * 64 + lane_e];              \
+          }                                                                             \
+          _Pragma("unroll") for (int j = 0; j < 4; ++j) {                               \
+            const int m = 8 * q + 4 * lhe + j;                                          \
+            if (m < te.nrows)                                                           \
+              store_h(h + (size_t)(te.row0 + m) * ldc + te.n0 + 32 * qb + lne,          \
+                      silu(gs[j]) * us[j]);                                             \
+          }                                                                             \
         }                                                                               \
-        const int m = 8 * (r >> 2) + 4 * lhe + (r & 3);                                 \
-        if (m < te.nrows)                                                               \
-          store_h(h + (size_t)(te.row0 + m) * ldc + te.n0 + 32 * qb + lne,              \
-                  silu(gs) * us);                                                       \
       }                                                                                 \
     } else {                                                                            \
       float* y = static_cast<float*>(c_out);                                            \
-      _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                  \
-        float ys = 0.0f;                                                                \
-        _Pragma("unroll") for (int w2 = 0; w2 < kSkWaves; ++w2)                         \
-            ys += red[((w2 * kSkBlocks + wv) * 16 + r) * 64 + lane_e];                  \
-        const int m = 8 * (r >> 2) + 4 * lhe + (r & 3);                                 \
-        if (m < te.nrows) y[(size_t)(te.row0 + m) * ldc + te.n0 + 32 * wv + lne] = ys;  \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                   \
+        if (q < nq) {                                                                   \
+          f32x4 ys = {0.0f, 0.0f, 0.0f, 0.0f};                                          \
+          _Pragma("unroll") for (int w2 = 0; w2 < kSkWaves; ++w2)                       \
+              ys += red4[((w2 * kSkBlocks + wv) * 4 + q) * 64 + lane_e];                \
+          _Pragma("unroll") for (int j = 0; j < 4; ++j) {                               \
+            const int m = 8 * q + 4 * lhe + j;                                          \
+            if (m < te.nrows)                                                           \
+              y[(size_t)(te.row0 + m) * ldc + te.n0 + 32 * wv + lne] = ys[j];           \
+          }                                                                             \
+        }                                                                               \
       }                                                                                 \
     }                                                                                   \
     __syncthreads();                                                                    \
   } while (0)
 
-  if (tid == 0) s_tile[0] = atomicAdd(next_tile, 1u);
-  __syncthreads();
-  uint32_t t = __builtin_amdgcn_readfirstlane(s_tile[0]);
+  // A workgroup's first tile is its own index, later ones come from the counter offset by
+  // the grid: every tile is taken once, without the grid's atomics on one address at the
+  // start.
+  uint32_t t = blockIdx.x;
   int par = 0;
   bool pre = false;   // this tile's first chunk (pair) was fetched during the previous one
+  int n_src = 0;          // A row of the next tile (loaded with its first weights)
+  uint32_t n_aoff = 0;    // its byte offset, computed in the epilogue
 
   // bf16 tiles: every tile of a bf16 layer; in an MXFP4 layer the shared experts' tiles,
   // which the counter hands out before all routed (MXFP4) ones.  Each phase carries only
@@ -754,7 +784,8 @@ void grouped_gemm_skinny_kernel(
     const uint32_t logical = ntiles - 1 - t;
     const SkTile tl = sk_tile<MODE>(plan, logical, NT);
     if (FP4 && tl.g < E) break;
-    const uint32_t a_voff = sk_a_row<MODE>(row_token, tl, ln, T, lda) + 64 * lh;
+    const uint32_t a_voff =
+        pre ? n_aoff : sk_a_off<MODE>(sk_a_src<MODE>(row_token, tl, ln), T, lda) + 64 * lh;
     uint32_t nxt = 0, tn = 0;   // next tile (nxt: lane 0 of wave 0 only)
     bool pre_n = false;         // its first chunk is fetched below
     SkTile ntl{0, 0, 1, 0};
@@ -769,7 +800,7 @@ void grouped_gemm_skinny_kernel(
     }
     int i = 0;
     for (; i + 2 < nw; i += 2) {
-      if (i + 4 >= nw && tid == 0) nxt = atomicAdd(next_tile, 1u);
+      if (i + 4 >= nw && tid == 0) nxt = gridDim.x + atomicAdd(next_tile, 1u);
       MOE_SKB_CODES(i + 1, 1, src);
       MOE_SKB_ROWS(i + 1, 1, a_voff);
       MOE_SKB_MMA(i, 0);
@@ -777,7 +808,7 @@ void grouped_gemm_skinny_kernel(
       MOE_SKB_ROWS(i + 2, 0, a_voff);
       MOE_SKB_MMA(i + 1, 1);
     }
-    if (nw == 2 && tid == 0) nxt = atomicAdd(next_tile, 1u);
+    if (nw == 2 && tid == 0) nxt = gridDim.x + atomicAdd(next_tile, 1u);
     MOE_SK_PUBLISH();
     MOE_SKB_CODES(i + 1, 1, src);
     MOE_SKB_ROWS(i + 1, 1, a_voff);
@@ -785,6 +816,7 @@ void grouped_gemm_skinny_kernel(
     if (tn < ntiles) {   // bc[0] is free once chunk i is in LDS
       ntl = sk_tile<MODE>(plan, ntiles - 1 - tn, NT);
       if (!FP4 || ntl.g >= E) {
+        n_src = sk_a_src<MODE>(row_token, ntl, ln);
         MOE_SKB_CODES(0, 0, b_src(ntl));
         pre_n = true;
       }
@@ -802,7 +834,8 @@ void grouped_gemm_skinny_kernel(
     while (t < ntiles) {
       const uint32_t logical = ntiles - 1 - t;
       const SkTile tl = sk_tile<MODE>(plan, logical, NT);
-      const uint32_t a_voff = sk_a_row<MODE>(row_token, tl, ln, T, lda) + 64 * lh;
+      const uint32_t a_voff =
+          pre ? n_aoff : sk_a_off<MODE>(sk_a_src<MODE>(row_token, tl, ln), T, lda) + 64 * lh;
       uint32_t nxt = 0, tn = 0;
       bool pre_n = false;
       SkTile ntl{0, 0, 1, 0};
@@ -818,19 +851,20 @@ void grouped_gemm_skinny_kernel(
       }
       int i = 0;
       for (; i + 2 < nw; i += 2) {
-        if (i + 4 >= nw && tid == 0) nxt = atomicAdd(next_tile, 1u);
+        if (i + 4 >= nw && tid == 0) nxt = gridDim.x + atomicAdd(next_tile, 1u);
         MOE_SKQ_ROWS(i + 1, 1, a_voff);
         MOE_SKQ_MMA(i, 0);
         MOE_SKQ_CODES(i + 2, src);
         MOE_SKQ_ROWS(i + 2, 0, a_voff);
         MOE_SKQ_MMA(i + 1, 1);
       }
-      if (nw == 2 && tid == 0) nxt = atomicAdd(next_tile, 1u);
+      if (nw == 2 && tid == 0) nxt = gridDim.x + atomicAdd(next_tile, 1u);
       MOE_SK_PUBLISH();
       MOE_SKQ_ROWS(i + 1, 1, a_voff);
       MOE_SKQ_MMA(i, 0);
       if (tn < ntiles) {   // qc and qs are free once chunk pair i is in LDS
         ntl = sk_tile<MODE>(plan, ntiles - 1 - tn, NT);
+        n_src = sk_a_src<MODE>(row_token, ntl, ln);
         MOE_SKQ_CODES(0, q_src(ntl));
         pre_n = true;
       }
