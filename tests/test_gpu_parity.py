@@ -76,6 +76,10 @@ SMALL = {c.name: c for c in [
     # next tile is taken and prefetched inside the K loop
     small("dec_soft_bf16_noshared", "softmax", "bf16", T=24, d=1024, E=32, S=0, I=256,
           k=8, seed=38),
+    # decode tiles whose groups hold 8 to 30 rows: one to four row quads of the
+    # accumulators exchanged between the waves
+    small("dec_sig_bf16_rows", "sigmoid", "bf16", T=30, d=512, E=8, S=1, I=256, k=4,
+          seed=42),
     # the tiling boundaries: 33 tokens, one past the decode tiles (128-row tiles), and
     # 256 tokens, the largest batch the one-workgroup permute takes
     small("sig_bf16_t33", "sigmoid", "bf16", T=33, d=512, E=24, S=2, I=256, k=6, seed=40),
@@ -121,6 +125,9 @@ MXFP4 = {c.name: c for c in [
     # pairs per wave (d = 2048)
     small("mx_dec_noshared", "softmax", "bf16", T=16, d=2048, E=24, S=0, I=512, k=6,
           seed=39).with_(weight_format="mxfp4"),
+    # decode tiles whose groups hold 8 to 30 rows (one to four row quads)
+    small("mx_dec_rows", "sigmoid", "bf16", T=30, d=512, E=8, S=1, I=256, k=4,
+          seed=43).with_(weight_format="mxfp4"),
     small("mx_sig_rows", "sigmoid", "bf16", T=400, d=256, E=6, S=1, I=256, k=2,
           seed=30).with_(weight_format="mxfp4"),
     small("mx_soft", "softmax", "bf16", T=100, d=512, E=12, S=0, I=128, k=3,
