@@ -79,7 +79,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", nargs="*", default=DEFAULT_WORKLOADS)
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU leg (oracle routing counts and the oracle timing)")
@@ -97,7 +97,10 @@ def layer_flops(c):
     return router, experts
 
 
-def run(c, steps, warmup, torch):
+def run(c, steps, warmup, torch, warm_s=0.0):
+    """Time `steps` steps of workload c after `warmup` untimed ones (and, when warm_s > 0,
+    further untimed steps until warm_s seconds of them have run: a decode step lasts
+    ~0.5-1.3 ms, and the GPU's clocks settle only after some hundred of them)."""
     import numpy as np
 
     from moe_inputs import make_inputs
@@ -121,6 +124,12 @@ def run(c, steps, warmup, torch):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    warm_steps, tw = warmup, time.perf_counter()
+    while time.perf_counter() - tw < warm_s:
+        for _ in range(10):
+            step()
+        warm_steps += 10
+        torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -143,7 +152,7 @@ def run(c, steps, warmup, torch):
     ms = wall * 1e3 / steps
     grouped_ms = float(stage[:, 2].mean())
     res = {
-        "T": T, "ms_per_step": ms, "tokens_per_s": T * steps / wall,
+        "T": T, "warmup_steps": warm_steps, "ms_per_step": ms, "tokens_per_s": T * steps / wall,
         "event_ms_per_step_median": float(np.median(step_ms)),
         "event_ms_per_step_p10": float(np.percentile(step_ms, 10)),
         "event_ms_per_step_p90": float(np.percentile(step_ms, 90)),
@@ -257,10 +266,11 @@ def main():
     head = args.workload[0]
     for name in args.workload:
         c = CONFIGS[name]
-        # The line's own workload times exactly --steps steps; a small batch beside it
-        # takes at least 50 (each of its steps is ~1 ms or less).
+        # The line's own workload times exactly --steps steps after exactly --warmup
+        # untimed ones; a small batch beside it times at least 50 (each of its steps is
+        # ~1 ms or less), and every workload beside it warms up for at least 0.5 s.
         steps = args.steps if (name == head or c.T >= 1024) else max(args.steps, 50)
-        res, inp = run(c, steps, args.warmup, torch)
+        res, inp = run(c, steps, args.warmup, torch, 0.0 if name == head else 0.5)
         res["steps"] = steps
         if not args.no_cpu_baseline:
             t0 = time.perf_counter()
@@ -300,7 +310,7 @@ def main():
         block = {
             "workload": name, "T": d["T"], "d": cc.d, "E": cc.E, "S": cc.S, "I": cc.I,
             "k": cc.k, "router": cc.router, "dtype": cc.dtype,
-            "weights": cc.weight_format, "steps": d["steps"],
+            "weights": cc.weight_format, "steps": d["steps"], "warmup_steps": d["warmup_steps"],
             "tokens_per_s": d["tokens_per_s"], "ms_per_step": d["ms_per_step"],
             "step_ms_p10_p50_p90": [d["event_ms_per_step_p10"], d["event_ms_per_step_median"],
                                     d["event_ms_per_step_p90"]],
