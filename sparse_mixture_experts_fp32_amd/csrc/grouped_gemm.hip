@@ -564,7 +564,9 @@ void grouped_gemm_skinny_kernel(
   // swizzled by (row / 2) % 8.
   const uint32_t cq_voff = static_cast<uint32_t>(lane >> 3) * (K / 2) + 16 * (lane & 7);
   const uint32_t cb_voff = static_cast<uint32_t>(lane >> 3) * K * 2 + 16 * (lane & 7);
-  const uint32_t s_voff = static_cast<uint32_t>(ln) * kMxRecBlocks;
+  // Scales: one 8-byte load per 64 B-rows, lane l taking B-row l of the record; a lane
+  // swap then gives every lane the bytes of its B-rows ln and ln + 32.
+  const uint32_t s_voff = static_cast<uint32_t>(lane) * kMxRecBlocks;
   char* stg = reinterpret_cast<char*>(red) + wv * (kSkBlocks * 16 * 64 * 4);
   uint32_t w_off[2];
 #pragma unroll
@@ -589,7 +591,7 @@ void grouped_gemm_skinny_kernel(
   // during the previous tile's last one (below), so the registers of its buffer 0 carry
   // over from one tile to the next.
   u32x4 qa[2][8], qc[16];      // MXFP4: A of a chunk, codes of a chunk pair
-  u32x2 qs[kSkBlocks];         // MXFP4: scale bytes of a chunk pair
+  u32x2 qs[kSkBlocks / 2];     // MXFP4: scale bytes of a chunk pair, B-row lane of a record
   u32x4 ba[2][4], bc[2][16];   // bf16: A and B of a chunk
 
   // B-row of this lane in block b, relative to its source's tile base: ln + bro(b).
@@ -603,12 +605,10 @@ void grouped_gemm_skinny_kernel(
     _Pragma("unroll") for (int q = 0; q < 16; ++q)                                      \
         qc[q] = load16<kStream>((MODE == 0 && q >= 8) ? (SRC).q1 : (SRC).q0, cq_voff,   \
                                 8 * (MODE == 0 ? (q & 7) : q) * (K / 2) + c_ * 64);     \
-    _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                               \
-        qs[b] = __builtin_amdgcn_raw_buffer_load_b64(                                   \
-            (MODE == 0 && b >= 2) ? (SRC).s1 : (SRC).s0, s_voff,                        \
-            ((MOE_SK_BRO(b) >> 6) * KR + (c_ >> 1)) * kMxRecBytes +                     \
-                (MOE_SK_BRO(b) & 63) * kMxRecBlocks,                                    \
-            0);                                                                         \
+    _Pragma("unroll") for (int r = 0; r < kSkBlocks / 2; ++r)                           \
+        qs[r] = __builtin_amdgcn_raw_buffer_load_b64(                                   \
+            (MODE == 0 && r == 1) ? (SRC).s1 : (SRC).s0, s_voff,                        \
+            ((MOE_SK_BRO(2 * r) >> 6) * KR + (c_ >> 1)) * kMxRecBytes, 0);              \
   } while (0)
   // A of iteration i into qa[P], rows at AV.
 #define MOE_SKQ_ROWS(i, P, AV)                                                          \
@@ -621,13 +621,21 @@ void grouped_gemm_skinny_kernel(
   do {                                                                                  \
     if (MOE_SKQ_CHUNK(i) < nchq) {                                                      \
       uint32_t sw_[kSkBlocks];                                                          \
-      _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                           \
-        if ((P) == 0) {                                                                 \
-          sw_[b] = qs[b][0];                                                            \
-          rs_hi[b] = qs[b][1];                                                          \
-        } else {                                                                        \
-          sw_[b] = rs_hi[b];                                                            \
+      if ((P) == 0) {                                                                   \
+        /* Blocks 2 r and 2 r + 1 are B-rows 0..31 and 32..63 of record r: */          \
+        /* swapping lane halves gives each lane both of its rows. */                    \
+        _Pragma("unroll") for (int r = 0; r < kSkBlocks / 2; ++r) {                     \
+          const auto lo_ = __builtin_amdgcn_permlane32_swap(qs[r][0], qs[r][0],         \
+                                                            false, false);              \
+          const auto hi_ = __builtin_amdgcn_permlane32_swap(qs[r][1], qs[r][1],         \
+                                                            false, false);              \
+          sw_[2 * r] = lo_[0];                                                          \
+          sw_[2 * r + 1] = lo_[1];                                                      \
+          rs_hi[2 * r] = hi_[0];                                                        \
+          rs_hi[2 * r + 1] = hi_[1];                                                    \
         }                                                                               \
+      } else {                                                                          \
+        _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) sw_[b] = rs_hi[b];        \
       }                                                                                 \
       if ((P) == 0) {                                                                   \
         _Pragma("unroll") for (int q = 0; q < 16; ++q)                                  \
