@@ -46,11 +46,18 @@ GROUPED_SOURCES = ["grouped_gemm.hip", "moe_device.h", "moe_launch.h"]
 
 
 def grouped_sources_sha256() -> str:
+    """sha256 of the grouped GEMM's sources with their comments and blank lines removed:
+    it changes when the compiled kernels can, not when only their comments do."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in GROUPED_SOURCES:
-        with open(os.path.join(ROOT, "sparse_mixture_experts_fp32_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_mixture_experts_fp32_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()
 
 

@@ -1090,8 +1090,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
   } while (0)
 
     // Halves 0, 1, 2 (B and A of step 0, B of step 1); wait for halves 0 and 1.  During
-    // step kt the wave issues halves 2kt + 3 (A of step kt + 1, two loads in each of
-    // substeps 0 and 1) and 2kt + 4 (B of step kt + 2, substeps 2 and 3), into the slots
+    // step kt a loader wave issues halves 2kt + 3 (A of step kt + 1, kWNB / 2 loads in
+    // each of substeps 0 and 1) and 2kt + 4 (B of step kt + 2, substeps 2 and 3), into the slots
     // that the barrier ending step kt - 1 freed; spreading them over the step keeps the
     // L1's miss queue busy without stalling a wave's MFMA issue on a burst of loads.
     MOE_WLOAD_B(0, 0);
