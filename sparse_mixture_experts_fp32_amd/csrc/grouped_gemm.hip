@@ -1081,12 +1081,15 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
   } while (0)
 
     bf16x8 fa[2][4], fb[2][2];
+  // In the order the MFMAs use them (row block 0 with both B-row blocks first), so the
+  // first MFMAs of a substep wait for three of the six reads, not five.
 #define MOE_WLOADF(sa, sb, s, buf)                                                      \
   do {                                                                                  \
-    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                    \
+    fa[buf][0] = Mfma<TE>::frag((sa), arow[0], (s), lane);                              \
+    fb[buf][0] = Mfma<TE>::frag((sb), brow[0], (s), lane);                              \
+    fb[buf][1] = Mfma<TE>::frag((sb), brow[1], (s), lane);                              \
+    _Pragma("unroll") for (int mi = 1; mi < 4; ++mi)                                    \
         fa[buf][mi] = Mfma<TE>::frag((sa), arow[mi], (s), lane);                        \
-    _Pragma("unroll") for (int ni = 0; ni < 2; ++ni)                                    \
-        fb[buf][ni] = Mfma<TE>::frag((sb), brow[ni], (s), lane);                        \
   } while (0)
 
     // Halves 0, 1, 2 (B and A of step 0, B of step 1); wait for halves 0 and 1.  During
