@@ -65,3 +65,23 @@ def test_committed_summaries_carry_traffic_and_sources_hash():
         assert len(fields["sources_sha256"]) == 64, p
         with open(p) as f:
             assert "rocprofv3" in f.read(), p
+
+
+def test_sources_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    csrc = tmp_path / "sparse_mixture_experts_fp32_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    body = {
+        "grouped_gemm.hip": "// header\nint f(int x) {\n  return x + 1;  // add one\n}\n",
+        "moe_device.h": "/* device\n   helpers */\n#define A 1\n",
+        "moe_launch.h": "#define B 2\n",
+    }
+    for name, text in body.items():
+        (csrc / name).write_text(text)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.grouped_sources_sha256()
+    (csrc / "grouped_gemm.hip").write_text(
+        "// header, reworded\n\nint f(int x) {\n  return x + 1;  // plus one\n}\n")
+    (csrc / "moe_device.h").write_text("/* other words */\n#define A 1\n")
+    assert bench.grouped_sources_sha256() == h0
+    (csrc / "grouped_gemm.hip").write_text("// header\nint f(int x) {\n  return x + 2;\n}\n")
+    assert bench.grouped_sources_sha256() != h0
