@@ -941,7 +941,8 @@ constexpr int kWSlots = 5;                // 160 KB, the whole LDS of a CU
 constexpr bool kPhaseSync = true;
 constexpr int kWLoadWaves = 4;            // waves that issue the loads (4 or 8)
 constexpr int kWNB = 32 / kWLoadWaves;    // 1 KB blocks per loader wave per half
-constexpr int kSpinLimit = 4000;          // polls of a phase wait (~1.5 ms at most)
+constexpr uint32_t kSpinTicks = 20000;    // a phase wait ends after 200 us (100 MHz clock)
+constexpr int kSpinLimit = 100000;        // and after this many polls in any case
 
 
 template <int MODE>
@@ -994,16 +995,22 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
       // The XCD's workgroups start each phase together, so the tiles of a phase stay
       // within a few K steps of each other and share their weight and row halves
       // through the L2.  Phases 0..p hold 32 p tiles plus those of chunk 8 p + xcd (all
-      // 32 but in the list's last chunk).  The wait is bounded: a workgroup that waits
-      // kSpinLimit polls goes on alone.  (Measured on the Inkling prefill shape: faster
-      // for gate/up, slower for the shorter down tiles, which run unsynchronized.)
+      // 32 but in the list's last chunk).  The wait is bounded in time: a workgroup that
+      // has waited kSpinTicks of the 100 MHz real-time clock (a legitimate wait is the
+      // gap between the tiles of one phase, ~10 us on average, tens of us at most) goes
+      // on alone, so a workgroup that is not yet resident (another kernel holds its CU)
+      // costs each phase at most 200 us; a bound in polls (each an agent-scope load of
+      // ~1-2 us) allowed several ms.  (Measured on the Inkling prefill shape: faster for
+      // gate/up, slower for the shorter down tiles, which run unsynchronized.)
       if (tid == 0) {
         __hip_atomic_fetch_add(sync + xcd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t target =
             phase * per_xcd + min(per_xcd, ntiles - (phase * kXcds + xcd) * per_xcd);
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         for (int it = 0; it < kSpinLimit; ++it) {
           if (__hip_atomic_load(sync + xcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-              target)
+                  target ||
+              __builtin_amdgcn_s_memrealtime() - t0 >= kSpinTicks)
             break;
           __builtin_amdgcn_s_sleep(4);
         }
