@@ -496,7 +496,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
 // workgroup takes its next tile from the counter during its current tile's last chunks
 // and fetches the next tile's first chunk (pair), and the row index of its A rows, while
 // the last MFMAs and the epilogue run.
-constexpr int kSkBM = 32;                 // rows per m-tile
+constexpr int kSkBM = 32;                 // rows per m-tile (bf16 groups)
+constexpr int kSkBM16 = 16;               // rows per m-tile of MXFP4 groups
 constexpr int kSkWaves = 4;               // waves per workgroup (K split)
 constexpr int kSkBlocks = 4;              // 32-wide B-row blocks per tile (128 B-rows)
 
@@ -563,12 +564,12 @@ void grouped_gemm_skinny_kernel(
 
   // MXFP4 B: chunks of 128 K elements (64 code bytes and 4 scale bytes per B-row).  Wave
   // w takes the chunk pairs 8 p + 2 w, 8 p + 2 w + 1 (one 128-byte line of codes and 8
-  // scale bytes per B-row); iteration i of a wave is chunk 8 (i / 2) + 2 w + i % 2.  In
-  // the operand layout, part j of a chunk gives lane half hh of B-row n the code bytes
-  // 32 j + 16 hh .. +16, i.e. MX block 2 j + hh of the chunk; MFMA step (j, u) covers K
-  // elements 64 j + 32 hh + 8 u .. +8 of the chunk for A and B alike.  The record of 64
-  // B-rows x 8 MX blocks that holds the scales of chunk pair p of the tile's 64-row
-  // block s sits at (s * KR + p) * 512 from the tile's scale base.
+  // scale bytes per B-row); iteration i of a wave is chunk 8 (i / 2) + 2 w + i % 2.  The
+  // MXFP4 tiles hold 16 rows and run on v_mfma_f32_16x16x32_bf16 (below); their operand
+  // layout gives lane 16 g + r MX block g of the chunk (16 code bytes) of B-row r of each
+  // 16-row column block.  The record of 64 B-rows x 8 MX blocks that holds the scales of
+  // chunk pair p of the tile's 64-row block s sits at (s * KR + p) * 512 from the tile's
+  // scale base.
   const int nchq = K / 128;
   const int KR = static_cast<int>(mx_rec_k(K));
   const uint32_t qbytes = static_cast<uint32_t>(kRowsPerSrc * (K / 2));
@@ -611,7 +612,7 @@ void grouped_gemm_skinny_kernel(
   // Operand registers, double-buffered by chunk.  A tile's first chunk (pair) is fetched
   // during the previous tile's last one (below), so the registers of its buffer 0 carry
   // over from one tile to the next.
-  u32x4 qa[2][8], qc[16];      // MXFP4: A of a chunk, codes of a chunk pair
+  u32x4 qa[2][4], qc[16];      // MXFP4: A of a chunk (16 rows), codes of a chunk pair
   u32x2 qs[kSkBlocks / 2];     // MXFP4: scale bytes of a chunk pair, B-row lane of a record
   u32x4 ba[2][4], bc[2][16];   // bf16: A and B of a chunk
 
@@ -631,54 +632,62 @@ void grouped_gemm_skinny_kernel(
             (MODE == 0 && r == 1) ? (SRC).s1 : (SRC).s0, s_voff,                        \
             ((MOE_SK_BRO(2 * r) >> 6) * KR + (c_ >> 1)) * kMxRecBytes, 0);              \
   } while (0)
+  // MXFP4 tiles hold 16 rows (the plan cuts MXFP4 groups into 16-row m-tiles: a decode
+  // group holds a few rows, so 32-row tiles spent half their A loads and MFMAs on
+  // padding) and run on v_mfma_f32_16x16x32_bf16.  Lane l = 16 g + r takes A row r, B-row
+  // r of each 16-row column block cb (tile B-row 16 cb + r) and MX block g of the chunk:
+  // MFMA step u covers K elements 32 g + 8 u .. +8 of the chunk for A and B alike (exact:
+  // the product sums over K).  The output of block cb in lane l is column 16 cb + r, rows
+  // 4 g .. +4.
   // A of iteration i into qa[P], rows at AV.
-#define MOE_SKQ_ROWS(i, P, AV)                                                          \
+#define MOE_SKQ16_ROWS(i, P, AV)                                                        \
   do {                                                                                  \
     const uint32_t c_ = static_cast<uint32_t>(min(MOE_SKQ_CHUNK(i), nchq - 1));         \
-    _Pragma("unroll") for (int u = 0; u < 8; ++u)                                       \
-        qa[P][u] = load16(a_rsrc, (AV), c_ * 256 + 128 * (u >> 2) + 16 * (u & 3));      \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u)                                       \
+        qa[P][u] = load16(a_rsrc, (AV), c_ * 256 + 16 * u);                             \
   } while (0)
-#define MOE_SKQ_MMA(i, P)                                                               \
+  // The scale byte of column block cb's B-row in MX block 4 P + g comes from the lane of
+  // its record that loaded that B-row (ds_bpermute); chunk 1's bytes are kept packed in
+  // rsp past the next pair's fetch.  Column blocks 0..3 / 4..7 are records 0 / 1.
+#define MOE_SKQ16_MMA(i, P)                                                             \
   do {                                                                                  \
     if (MOE_SKQ_CHUNK(i) < nchq) {                                                      \
-      uint32_t sw_[kSkBlocks];                                                          \
-      if ((P) == 0) {                                                                   \
-        /* Blocks 2 r and 2 r + 1 are B-rows 0..31 and 32..63 of record r: */          \
-        /* swapping lane halves gives each lane both of its rows. */                    \
-        _Pragma("unroll") for (int r = 0; r < kSkBlocks / 2; ++r) {                     \
-          const auto lo_ = __builtin_amdgcn_permlane32_swap(qs[r][0], qs[r][0],         \
-                                                            false, false);              \
-          const auto hi_ = __builtin_amdgcn_permlane32_swap(qs[r][1], qs[r][1],         \
-                                                            false, false);              \
-          sw_[2 * r] = lo_[0];                                                          \
-          sw_[2 * r + 1] = lo_[1];                                                      \
-          rs_hi[2 * r] = hi_[0];                                                        \
-          rs_hi[2 * r + 1] = hi_[1];                                                    \
-        }                                                                               \
-      } else {                                                                          \
-        _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) sw_[b] = rs_hi[b];        \
-      }                                                                                 \
+      uint32_t sb_[8];                                                                  \
       if ((P) == 0) {                                                                   \
         _Pragma("unroll") for (int q = 0; q < 16; ++q)                                  \
             *reinterpret_cast<u32x4*>(stg + 1024 * q + w_off[q & 1]) = qc[q];           \
+        rsp[0] = 0u;                                                                    \
+        rsp[1] = 0u;                                                                    \
+        _Pragma("unroll") for (int cb = 0; cb < 8; ++cb) {                              \
+          const int src_ = (16 * (cb & 3) + r16) << 2;                                  \
+          const uint32_t w0_ = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(      \
+              src_, static_cast<int>(qs[cb >> 2][0])));                                 \
+          const uint32_t w1_ = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(      \
+              src_, static_cast<int>(qs[cb >> 2][1])));                                 \
+          sb_[cb] = (w0_ >> (8 * g16)) & 0xffu;                                         \
+          rsp[cb >> 2] |= ((w1_ >> (8 * g16)) & 0xffu) << (8 * (cb & 3));               \
+        }                                                                               \
+      } else {                                                                          \
+        _Pragma("unroll") for (int cb = 0; cb < 8; ++cb)                                \
+            sb_[cb] = (rsp[cb >> 2] >> (8 * (cb & 3))) & 0xffu;                         \
       }                                                                                 \
-      _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                   \
-        u32x4 cq_[kSkBlocks];                                                           \
-        _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                           \
-            cq_[b] = *reinterpret_cast<const u32x4*>(                                   \
-                stg + 4096 * b + 128 * ln +                                             \
-                16 * ((4 * (P) + 2 * j + lh) ^ ((ln >> 1) & 7)));                       \
-        float sc_[kSkBlocks];                                                           \
-        _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b)                           \
-            sc_[b] = mx_scale(sw_[b] >> (8 * (2 * j + lh)));                            \
+      _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_) {                                \
+        u32x4 cq_[4];                                                                   \
+        float sc_[4];                                                                   \
+        _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                 \
+          cq_[c] = *reinterpret_cast<const u32x4*>(stg + lq16[P] + 2048 * (4 * h_ + c));\
+          sc_[c] = mx_scale(sb_[4 * h_ + c]);                                           \
+        }                                                                               \
         _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                 \
-          const bf16x8 fa_ = __builtin_bit_cast(bf16x8, qa[P][4 * j + u]);              \
-          _Pragma("unroll") for (int b = 0; b < kSkBlocks; ++b) {                       \
+          __builtin_amdgcn_sched_barrier(0);                                            \
+          _Pragma("unroll") for (int c = 0; c < 4; ++c) {                               \
             const bf16x8 fb_ =                                                          \
-                __builtin_bit_cast(bf16x8, mxfp4_chunk(cq_[b][u], sc_[b]));             \
-            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_, fb_, acc[b], 0, 0, 0);\
+                __builtin_bit_cast(bf16x8, mxfp4_chunk(cq_[c][u], sc_[c]));             \
+            acc16[4 * h_ + c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                \
+                __builtin_bit_cast(bf16x8, qa[P][u]), fb_, acc16[4 * h_ + c], 0, 0, 0); \
           }                                                                             \
         }                                                                               \
+        __builtin_amdgcn_sched_barrier(0);                                              \
       }                                                                                 \
     }                                                                                   \
   } while (0)
@@ -797,6 +806,57 @@ void grouped_gemm_skinny_kernel(
     __syncthreads();                                                                    \
   } while (0)
 
+  // The epilogue of the 16-row MXFP4 tiles: partial sums -> LDS as the accumulator
+  // quads ([wave][column block][lane], in the wave's own 16 KB, which only it read in the
+  // K loop: no wave writes where another may still be reading codes); then gate/up wave
+  // w forms h columns 16 w .. +16 (gate block w, up block w + 4) and down wave w outputs
+  // column blocks 2 w and 2 w + 1, adding the four waves' partials in wave order; plus
+  // the next tile's first A rows at n_aoff.
+#define MOE_SK16_EPILOGUE()                                                             \
+  do {                                                                                  \
+    int lane_e = lane;                                                                  \
+    uint32_t lg_ = logical;                                                             \
+    asm volatile("" : "+v"(lane_e), "+s"(lg_));                                         \
+    const int re = lane_e & 15, ge = lane_e >> 4;                                       \
+    const SkTile te = sk_tile<MODE>(plan, lg_, NT);                                     \
+    f32x4* red4 = reinterpret_cast<f32x4*>(red);                                        \
+    f32x4* mine = red4 + wv * (16 * 64);   /* this wave's own 16 KB */                  \
+    _Pragma("unroll") for (int cb = 0; cb < 8; ++cb) mine[cb * 64 + lane_e] = acc16[cb];\
+    __syncthreads();                                                                    \
+    if (pre_n) {                                                                        \
+      n_aoff = sk_a_off<MODE>(n_src, T, lda) + 64 * (lane_e >> 4);                      \
+      MOE_SKQ16_ROWS(0, 0, n_aoff);                                                     \
+    }                                                                                   \
+    if (MODE == 0) {                                                                    \
+      uint16_t* h = static_cast<uint16_t*>(c_out);                                      \
+      f32x4 gs = {0.0f, 0.0f, 0.0f, 0.0f}, us = gs;                                     \
+      _Pragma("unroll") for (int w2 = 0; w2 < kSkWaves; ++w2) {                         \
+        gs += red4[(w2 * 16 + wv) * 64 + lane_e];                                        \
+        us += red4[(w2 * 16 + wv + 4) * 64 + lane_e];                                    \
+      }                                                                                 \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                   \
+        const int m = 4 * ge + j;                                                       \
+        if (m < te.nrows)                                                               \
+          store_h(h + (size_t)(te.row0 + m) * ldc + te.n0 + 16 * wv + re,               \
+                  silu(gs[j]) * us[j]);                                                 \
+      }                                                                                 \
+    } else {                                                                            \
+      float* y = static_cast<float*>(c_out);                                            \
+      _Pragma("unroll") for (int cc = 0; cc < 2; ++cc) {                                \
+        const int cb = 2 * wv + cc;                                                     \
+        f32x4 ys = {0.0f, 0.0f, 0.0f, 0.0f};                                            \
+        _Pragma("unroll") for (int w2 = 0; w2 < kSkWaves; ++w2)                         \
+            ys += red4[(w2 * 16 + cb) * 64 + lane_e];                                    \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                 \
+          const int m = 4 * ge + j;                                                     \
+          if (m < te.nrows)                                                             \
+            y[(size_t)(te.row0 + m) * ldc + te.n0 + 16 * cb + re] = ys[j];              \
+        }                                                                               \
+      }                                                                                 \
+    }                                                                                   \
+    __syncthreads();                                                                    \
+  } while (0)
+
   // A workgroup's first tile is its own index, later ones come from the counter offset by
   // the grid: every tile is taken once, without the grid's atomics on one address at the
   // start.
@@ -857,60 +917,70 @@ void grouped_gemm_skinny_kernel(
     pre = pre_n;
   }
 
-  // MXFP4 tiles (every tile after them is one as well).
+  // MXFP4 tiles (every tile after them is one as well), on 16-row MFMA blocks.
   if (FP4) {
+    const int r16 = lane & 15, g16 = lane >> 4;
+    // LDS offset of this lane's 16 code bytes in column block 0, per chunk of a pair
+    // (B-row r16, MX block g16, slot swizzled by (row / 2) % 8; block cb adds 2048 cb).
+    uint32_t lq16[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      lq16[c] = 128 * r16 + 16 * ((4 * c + g16) ^ ((r16 >> 1) & 7));
+      asm volatile("" : "+v"(lq16[c]));
+    }
     pre = false;
     while (t < ntiles) {
       const uint32_t logical = ntiles - 1 - t;
       const SkTile tl = sk_tile<MODE>(plan, logical, NT);
       const uint32_t a_voff =
-          pre ? n_aoff : sk_a_off<MODE>(sk_a_src<MODE>(row_token, tl, ln), T, lda) + 64 * lh;
+          pre ? n_aoff : sk_a_off<MODE>(sk_a_src<MODE>(row_token, tl, r16), T, lda) + 64 * g16;
       uint32_t nxt = 0, tn = 0;
       bool pre_n = false;
       SkTile ntl{0, 0, 1, 0};
-      f32x16 acc[kSkBlocks];
+      f32x4 acc16[8];
 #pragma unroll
-      for (int b = 0; b < kSkBlocks; ++b) acc[b] = f32x16{};
+      for (int cb = 0; cb < 8; ++cb) acc16[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       const int nw = 2 * ((nchq + 2 * kSkWaves - 1) / (2 * kSkWaves));
       const SkQSrc src = q_src(tl);
-      uint32_t rs_hi[kSkBlocks];     // the pair's second chunk, kept past the next fetch
+      uint32_t rsp[2];   // chunk 1's scale bytes of a pair, kept past the next fetch
       if (!pre) {
         MOE_SKQ_CODES(0, src);
-        MOE_SKQ_ROWS(0, 0, a_voff);
+        MOE_SKQ16_ROWS(0, 0, a_voff);
       }
       int i = 0;
       for (; i + 2 < nw; i += 2) {
         if (i + 4 >= nw && tid == 0) nxt = gridDim.x + atomicAdd(next_tile, 1u);
-        MOE_SKQ_ROWS(i + 1, 1, a_voff);
-        MOE_SKQ_MMA(i, 0);
+        MOE_SKQ16_ROWS(i + 1, 1, a_voff);
+        MOE_SKQ16_MMA(i, 0);
         MOE_SKQ_CODES(i + 2, src);
-        MOE_SKQ_ROWS(i + 2, 0, a_voff);
-        MOE_SKQ_MMA(i + 1, 1);
+        MOE_SKQ16_ROWS(i + 2, 0, a_voff);
+        MOE_SKQ16_MMA(i + 1, 1);
       }
       if (nw == 2 && tid == 0) nxt = gridDim.x + atomicAdd(next_tile, 1u);
       MOE_SK_PUBLISH();
-      MOE_SKQ_ROWS(i + 1, 1, a_voff);
-      MOE_SKQ_MMA(i, 0);
+      MOE_SKQ16_ROWS(i + 1, 1, a_voff);
+      MOE_SKQ16_MMA(i, 0);
       if (tn < ntiles) {   // qc and qs are free once chunk pair i is in LDS
         ntl = sk_tile<MODE>(plan, ntiles - 1 - tn, NT);
-        n_src = sk_a_src<MODE>(row_token, ntl, ln);
+        n_src = sk_a_src<MODE>(row_token, ntl, r16);
         MOE_SKQ_CODES(0, q_src(ntl));
         pre_n = true;
       }
-      MOE_SKQ_MMA(i + 1, 1);
-      MOE_SK_EPILOGUE(MOE_SKQ_ROWS);
+      MOE_SKQ16_MMA(i + 1, 1);
+      MOE_SK16_EPILOGUE();
       t = tn;
       par ^= 1;
       pre = pre_n;
     }
   }
 #undef MOE_SK_EPILOGUE
+#undef MOE_SK16_EPILOGUE
+#undef MOE_SKQ16_MMA
+#undef MOE_SKQ16_ROWS
 #undef MOE_SK_PUBLISH
 #undef MOE_SKB_MMA
 #undef MOE_SKB_ROWS
 #undef MOE_SKB_CODES
-#undef MOE_SKQ_MMA
-#undef MOE_SKQ_ROWS
 #undef MOE_SKQ_CODES
 #undef MOE_SKQ_CHUNK
 #undef MOE_SK_BRO
@@ -1228,18 +1298,20 @@ __global__ __launch_bounds__(512) void grouped_gemm_wide_kernel(
 }
 
 // m-tile plan: plan[0].group = number of m-tiles; plan[1 + i] = the i-th m-tile, groups in
-// order, BM rows each except a group's last; .pad holds the group's first m-tile.
+// order, BM rows each (16 for groups g < E16: the MXFP4 decode tiles) except a group's
+// last; .pad holds the group's first m-tile.
 template <int BM>
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets,
                                                     int G, PlanEntry* __restrict__ plan,
-                                                    uint32_t* __restrict__ sync) {
+                                                    uint32_t* __restrict__ sync, int E16) {
   __shared__ int32_t scan[1024];
   const int g = threadIdx.x;
   if (g < 4 * kSyncEntries) sync[g] = 0;
+  const int bm = g < E16 ? kSkBM16 : BM;   // groups g < E16: 16-row m-tiles
   int c = 0, m = 0;
   if (g < G) {
     c = offsets[g + 1] - offsets[g];
-    m = (c + BM - 1) / BM;
+    m = (c + bm - 1) / bm;
   }
   scan[g] = m;
   __syncthreads();
@@ -1254,7 +1326,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (g < G) {
     const int r0 = offsets[g];
     for (int i = 0; i < m; ++i)
-      plan[1 + start + i] = PlanEntry{g, r0 + i * BM, min(BM, c - i * BM), start};
+      plan[1 + start + i] = PlanEntry{g, r0 + i * bm, min(bm, c - i * bm), start};
   }
 }
 
@@ -1331,7 +1403,7 @@ static hipError_t launch_skinny(const uint16_t* x, const int32_t* offsets,
   uint32_t* sync = reinterpret_cast<uint32_t*>(plan + 1 + max_mtiles(R, G));
   const int hp = static_cast<int>(h_pitch(I));
   hipLaunchKernelGGL(plan_kernel<kSkBM>, dim3(1), dim3(1024), 0, stream, offsets, G, plan,
-                     sync);
+                     sync, FP4 ? E : 0);
   hipLaunchKernelGGL((grouped_gemm_skinny_kernel<0, FP4>), dim3(grid), dim3(256), 0, stream,
                      x, row_token, wg, wu, q.codes_gate, q.codes_up, q.scales_gate,
                      q.scales_up, plan, sync, static_cast<void*>(h),
@@ -1383,7 +1455,7 @@ static hipError_t launch_typed(const TE* x, const int32_t* offsets, const int32_
     return hipGetLastError();
   }
   hipLaunchKernelGGL(plan_kernel<kBM>, dim3(1), dim3(1024), 0, stream, offsets, G, plan,
-                     sync);
+                     sync, 0);
   hipLaunchKernelGGL((grouped_gemm_kernel<TE, 0, false>), dim3(grid),
                      dim3(512), 0, stream, x, row_token, wg, wu, offsets, plan,
                      static_cast<void*>(h), static_cast<uint32_t>((size_t)T * d * sizeof(TE)),
@@ -1415,7 +1487,7 @@ hipError_t launch_grouped_swiglu_mxfp4(const uint16_t* x, const int32_t* offsets
   uint32_t* sync = reinterpret_cast<uint32_t*>(plan + 1 + max_mtiles(R, G));
   const int hp = static_cast<int>(h_pitch(I));
   hipLaunchKernelGGL(plan_kernel<kBM>, dim3(1), dim3(1024), 0, stream, offsets, G, plan,
-                     sync);
+                     sync, 0);
   hipLaunchKernelGGL((grouped_gemm_kernel<uint16_t, 0, true>), dim3(grid), dim3(512), 0,
                      stream, x, row_token, wg_shared, wu_shared, offsets, plan,
                      static_cast<void*>(h), static_cast<uint32_t>((size_t)T * d * 2), d, I, T,

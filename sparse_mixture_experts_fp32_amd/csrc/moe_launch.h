@@ -102,9 +102,9 @@ hipError_t launch_combine(const float* y_rows, const int32_t* slot_row, const fl
                           const float* residual, float* out, int T, int d, int A, int R,
                           hipStream_t stream);
 
-// Upper bound of the grouped GEMM's m-tiles for R rows in G groups (the smallest m-tile
-// has 32 rows).
-constexpr int kMinTileRows = 32;
+// Upper bound of the grouped GEMM's m-tiles for R rows in G groups (the smallest m-tile,
+// that of the MXFP4 decode tiles, has 16 rows).
+constexpr int kMinTileRows = 16;
 inline int64_t max_mtiles(int64_t R, int64_t G) { return R / kMinTileRows + G; }
 
 // Row pitch (elements) of the intermediate h [R, I]: 64 elements of padding per row, so
