@@ -15,11 +15,11 @@
 //     groups average fewer than 128 rows, with more than 32 tokens;
 //   - 256 x 256 (grouped_gemm_wide_kernel): bf16 layers whose groups average 128 rows or
 //     more;
-//   - 32 x 128 with K split over four waves (grouped_gemm_skinny_kernel): bf16 layers of
-//     at most 32 tokens, where the step streams weights.
+//   - 32 x 128 with K split over four waves (grouped_gemm_skinny_kernel; 16 x 128 for
+//     MXFP4 groups): bf16 layers of at most 32 tokens, where the step streams weights.
 // Routed experts may hold MXFP4 weights (4-bit codes, one power-of-two scale per 32
 // elements along K, the scales packed in records of 64 rows x 8 MX blocks); the 128-row
-// and 32-row tilings expand them to bf16 on the way to the MFMAs.
+// and decode tilings expand them to bf16 on the way to the MFMAs.
 //
 // Work decomposition (128-row tiling).  A device-built plan lists the m-tiles (up to 128
 // rows of one group).  Tiles are ordered group by group; inside a group in blocks of 4
@@ -476,8 +476,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
 
 // ---- Decode-shaped tiles (bf16 layers with at most 32 tokens)
 //
-// Every group then has at most 32 rows, so one 32-row m-tile per group, and the step is
-// bound by streaming the experts' weights.  A tile is 32 rows x 128 B-rows (gate/up: 64
+// Every group then has at most 32 rows, so one 32-row m-tile per bf16 group (MXFP4 groups
+// take 16-row m-tiles, below), and the step is bound by streaming the experts' weights.
+// A tile is 32 (16) rows x 128 B-rows (gate/up: 64
 // gate + 64 up rows of the same h columns; down: 128 output columns); the 4 waves of a
 // workgroup split its K range into interleaved chunks, double-buffered in registers one
 // chunk ahead, and the K loop's only barrier is at its last chunk (below).  Weights are
@@ -488,8 +489,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(
 // so any order shared by A and B is exact) so that an A load is 16 contiguous bytes and
 // an MXFP4 operand is one MX block (16 bytes of codes, one scale byte).  MXFP4 codes are
 // converted to bf16 in registers.  Rows past the group's end load a copy of its last row
-// (their outputs are not stored).  The 4 waves' partial 32 x 128 sums are added in LDS
-// in wave order (only the row quads that hold rows of the group), then the SwiGLU
+// (their outputs are not stored).  The 4 waves' partial sums are added in LDS in wave
+// order (of 32-row tiles only the row quads that hold rows of the group), then the SwiGLU
 // (gate/up) or the f32 row store (down) runs.  Tiles are taken last plan m-tile first, so
 // the shared experts' bf16 tiles (about 4x the bytes of an MXFP4 tile) start before the
 // routed ones: a workgroup's first tile is its index, later ones come from a counter.  A
