@@ -125,7 +125,8 @@ MXFP4 = {c.name: c for c in [
     # pairs per wave (d = 2048)
     small("mx_dec_noshared", "softmax", "bf16", T=16, d=2048, E=24, S=0, I=512, k=6,
           seed=39).with_(weight_format="mxfp4"),
-    # decode tiles whose groups hold 8 to 30 rows (one to four row quads)
+    # decode tiles whose groups hold 8 to 30 rows: three routed groups of 17 to 24 rows,
+    # each cut into two 16-row m-tiles (and mx_dec_soft has one of exactly 16)
     small("mx_dec_rows", "sigmoid", "bf16", T=30, d=512, E=8, S=1, I=256, k=4,
           seed=43).with_(weight_format="mxfp4"),
     small("mx_sig_rows", "sigmoid", "bf16", T=400, d=256, E=6, S=1, I=256, k=2,
