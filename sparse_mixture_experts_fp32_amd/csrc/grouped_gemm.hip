@@ -1388,8 +1388,9 @@ __global__ __launch_bounds__(1024) void plan_wide_kernel(const int32_t* __restri
   }
 }
 
-// Decode-shaped tiling: plan of 32-row m-tiles, then the gate/up and down kernels, each
-// taking tiles from its own counter (zeroed by the plan kernel).  Two workgroups per CU.
+// Decode-shaped tiling: plan of 32-row m-tiles (16-row for MXFP4 groups), then the gate/up
+// and down kernels, each taking tiles from its own counter (zeroed by the plan kernel).
+// Two workgroups per CU.
 template <bool FP4>
 static hipError_t launch_skinny(const uint16_t* x, const int32_t* offsets,
                                 const int32_t* row_token, const uint16_t* wg,

@@ -1,8 +1,8 @@
 // MXFP4 scale packing: E8M0 scale bytes [E, N, K/32] (row n, MX block kb) -> records of
 // kMxRecRows rows x kMxRecBlocks bytes, one per (expert, 64-row block of N, 8 MX blocks
-// of K), the order in which the grouped GEMMs read them.  A wave of the 32-row tiling then
-// fetches the scales of 32 B-rows for a 256-element K range as 256 contiguous bytes (two
-// cache lines) instead of one line per B-row.
+// of K), the order in which the grouped GEMMs read them.  A wave of the decode tiling then
+// fetches the scales of a record's 64 B-rows for a 256-element K range with one 8-byte
+// load per lane (512 contiguous bytes) instead of one line per B-row.
 #include "moe_launch.h"
 
 namespace moe {
